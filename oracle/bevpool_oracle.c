@@ -1,0 +1,180 @@
+/*
+ * CPU oracle for BEV pooling: TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, obviously-correct C used to check the HIP path.  Only the
+ * tests, the smoke check and the benchmark's CPU-baseline leg may load it;
+ * the product library never calls, links or includes anything here, and
+ * this file includes nothing from the product.
+ *
+ * Source: "Accelerating BEV Pooling on NVIDIA GPUs for Physical AI
+ * Applications" (NVIDIA technical blog; Vietnamese and Chinese copies).
+ *   - Section "Remove redundant scatter traffic": the operator is the
+ *     scatter-reduce  out[ranks_bev[t], c] += depth[ranks_depth[t]] *
+ *     feat[ranks_feat[t], c]  over scatter points t, and the scatter map is
+ *     five INT32 arrays (ranks_depth, ranks_feat, ranks_bev,
+ *     interval_starts, interval_lengths).
+ *   - Section "Implement the interval-owned scatter-reduce": the map is
+ *     prepared in advance; an interval is a run of points with the same
+ *     ranks_bev and its cell is ranks_bev[start]; every output cell is
+ *     written once.
+ * The pages leave the map's construction open.  Readings used here:
+ *   points are the frustum points whose cell is >= 0; they are ordered by
+ *   the key (cell, frustum index p), a total order, so the map is unique;
+ *   intervals are the maximal runs of equal cell in that order, listed in
+ *   increasing cell; ranks_depth[t] = p (depth is [img, D, H, W] flat) and
+ *   ranks_feat[t] = img * H * W + h * W + w (feat is [img, H, W, C]);
+ *   cells that own no interval are zero.
+ * Arithmetic: every value is decoded to double and summed in double in
+ * increasing t.  fp16 x fp16 and (e4m3 * fp32 scale) x fp16 products are
+ * exact in double, so only the double summation rounds.
+ *
+ * Pins (tests/test_oracle_pins.py): all 65536 fp16 and 256 e4m3 codes
+ * against numpy / torch and the format's closed form; the map against
+ * numpy.lexsort and a hand-worked example; the forward against a dense
+ * one-hot matrix product, closed forms and invariants.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_E4M3 = 2 };
+
+/* IEEE 754 binary16: sign, 5-bit exponent (bias 15), 10-bit fraction. */
+double oracle_decode_f16(uint16_t h)
+{
+    int sign = h >> 15;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);              /* subnormal: m/1024 * 2^-14 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp(1024.0 + m, e - 25);          /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* OCP 8-bit floating point, E4M3 ("FN": finite, no infinities):
+ * sign, 4-bit exponent (bias 7), 3-bit mantissa; S.1111.111 is NaN. */
+double oracle_decode_e4m3(uint8_t q)
+{
+    int sign = q >> 7;
+    int e = (q >> 3) & 0xf;
+    int m = q & 0x7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);               /* subnormal: m/8 * 2^-6 */
+    else
+        v = ldexp(8.0 + m, e - 10);             /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+static double load_value(const void *base, int dtype, int64_t i)
+{
+    switch (dtype) {
+    case ORACLE_F32: return (double)((const float *)base)[i];
+    case ORACLE_F16: return oracle_decode_f16(((const uint16_t *)base)[i]);
+    default:         return oracle_decode_e4m3(((const uint8_t *)base)[i]);
+    }
+}
+
+typedef struct { int64_t cell; int64_t p; } oracle_key;
+
+static int key_cmp(const void *a, const void *b)
+{
+    const oracle_key *x = (const oracle_key *)a, *y = (const oracle_key *)b;
+    if (x->cell != y->cell) return x->cell < y->cell ? -1 : 1;
+    if (x->p != y->p) return x->p < y->p ? -1 : 1;
+    return 0;
+}
+
+/*
+ * Scatter map from the per-point cell index.
+ * point_cell[p], p < n_img*D*H*W, is a cell in [0, n_cells) or -1 (dropped).
+ * Outputs need room for every kept point.  Returns 0, or -1 when a cell is
+ * out of range (outputs then undefined), or -2 when memory runs out.
+ */
+int oracle_build_map(const int32_t *point_cell, int64_t n_img, int64_t D,
+                     int64_t H, int64_t W, int64_t n_cells,
+                     int32_t *ranks_depth, int32_t *ranks_feat, int32_t *ranks_bev,
+                     int32_t *interval_starts, int32_t *interval_lengths,
+                     int64_t *n_points, int64_t *n_intervals)
+{
+    int64_t P = n_img * D * H * W;
+    int64_t N = 0;
+    for (int64_t p = 0; p < P; ++p) {
+        if (point_cell[p] < -1 || point_cell[p] >= n_cells) return -1;
+        if (point_cell[p] >= 0) ++N;
+    }
+    oracle_key *keys = (oracle_key *)malloc((size_t)(N > 0 ? N : 1) * sizeof(oracle_key));
+    if (!keys) return -2;
+    int64_t k = 0;
+    for (int64_t p = 0; p < P; ++p)
+        if (point_cell[p] >= 0) { keys[k].cell = point_cell[p]; keys[k].p = p; ++k; }
+
+    /* order the kept points by (cell, p) */
+    qsort(keys, (size_t)N, sizeof(oracle_key), key_cmp);
+
+    int64_t dhw = D * H * W, hw = H * W;
+    for (int64_t t = 0; t < N; ++t) {
+        int64_t p = keys[t].p;
+        ranks_bev[t] = (int32_t)keys[t].cell;
+        ranks_depth[t] = (int32_t)p;
+        ranks_feat[t] = (int32_t)((p / dhw) * hw + p % hw);   /* image, then (h, w) */
+    }
+    free(keys);
+
+    /* an interval starts wherever the cell changes */
+    int64_t I = 0;
+    for (int64_t t = 0; t < N; ++t)
+        if (t == 0 || ranks_bev[t] != ranks_bev[t - 1])
+            interval_starts[I++] = (int32_t)t;
+    for (int64_t i = 0; i < I; ++i)
+        interval_lengths[i] = (int32_t)((i + 1 < I ? interval_starts[i + 1] : N) - interval_starts[i]);
+
+    *n_points = N;
+    *n_intervals = I;
+    return 0;
+}
+
+/*
+ * The scatter-reduce itself, in double:
+ *   out[ranks_bev[t], c] = sum over t (increasing) of
+ *                          depth[ranks_depth[t]] * feat[ranks_feat[t], c]
+ * with e4m3 features read as e4m3(q) * feat_scale.  Cells no point maps to
+ * stay 0.  out_abs (optional) receives the same sum of |term|, the scale of
+ * the rounding-error bound of any summation order.
+ * out and out_abs are [n_cells, C].  Returns 0, or -1 on a bad dtype or an
+ * index outside the stated sizes.
+ */
+int oracle_forward(const void *depth, int depth_dtype, int64_t n_depth,
+                   const void *feat, int feat_dtype, int64_t n_feat_rows, int64_t C,
+                   double feat_scale,
+                   const int32_t *ranks_depth, const int32_t *ranks_feat,
+                   const int32_t *ranks_bev, int64_t n_points, int64_t n_cells,
+                   double *out, double *out_abs)
+{
+    if (depth_dtype < ORACLE_F32 || depth_dtype > ORACLE_F16) return -1;
+    if (feat_dtype < ORACLE_F32 || feat_dtype > ORACLE_E4M3) return -1;
+    double fscale = feat_dtype == ORACLE_E4M3 ? feat_scale : 1.0;
+
+    memset(out, 0, (size_t)(n_cells * C) * sizeof(double));
+    if (out_abs) memset(out_abs, 0, (size_t)(n_cells * C) * sizeof(double));
+
+    for (int64_t t = 0; t < n_points; ++t) {
+        int64_t rd = ranks_depth[t], rf = ranks_feat[t], rb = ranks_bev[t];
+        if (rd < 0 || rd >= n_depth || rf < 0 || rf >= n_feat_rows || rb < 0 || rb >= n_cells)
+            return -1;
+        double d = load_value(depth, depth_dtype, rd);
+        for (int64_t c = 0; c < C; ++c) {
+            double term = d * (load_value(feat, feat_dtype, rf * C + c) * fscale);
+            out[rb * C + c] += term;
+            if (out_abs) out_abs[rb * C + c] += fabs(term);
+        }
+    }
+    return 0;
+}

@@ -1,0 +1,210 @@
+"""Seeded synthetic inputs for BEV pooling.
+
+This module only *generates* inputs: camera-frustum geometry turned into a
+per-point BEV cell index, per-pixel depth distributions and image features.
+It holds none of the pooling arithmetic (no map building, no scatter-reduce,
+no fp8 decoding), so both the CPU oracle and the GPU path can take their
+inputs from it without sharing any of the method's code.
+
+Geometry.  Frustum point p enumerates (image, depth bin, row, column) as
+    p = ((img * D + d) * H + h) * W + w,    img = frame * n_cam + camera
+Camera n looks along yaw 60 deg * n with a 60 deg horizontal field of view;
+column w sits at azimuth yaw + (w / W - 0.5) * fov.  Depth bin d sits at
+range r_d = r0 + d * span / D.  The point lands at x = r cos(az),
+y = r sin(az) (the row h does not move it).  The BEV grid is G x G cells of
+side s centred on the cameras; ix = floor((x + G s / 2) / s), likewise iy,
+and a point is kept only when 0 <= ix, iy < G (half-open).  Its cell is
+frame * G*G + iy * G + ix, or -1 when dropped.  A Bernoulli draw then keeps
+each in-grid point with probability p_keep = target / in_grid_count, which
+brings the kept count near the stated workload size.
+
+Values.  rng = numpy.random.default_rng(seed), drawn in this order:
+depth logits [n_img, D, H, W] ~ N(0, 1), softmax over D in float64;
+features [n_img, H, W, C] ~ N(0, 1); uniforms u[P] for the Bernoulli keep.
+Storage casts use round-to-nearest-even.  The fp8 workload quantises the
+fp16 features of the BEVDet-like workload as e4m3(x * 448 / absmax) with
+the per-tensor scale absmax / 448 kept in fp32.
+
+The workload shapes stand in for the camera rig the BEV-pooling blog
+("Accelerating BEV Pooling on NVIDIA GPUs for Physical AI Applications",
+section "How BEVPoolV3 lowers latency") measures on: about 209K scatter
+points and 80 feature channels.  That rig's recorded driving data is not
+available here; these are synthetic stand-ins of the same size.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+__all__ = ["WorkloadSpec", "Workload", "SPECS", "spec", "make_workload",
+           "make_random_cells", "describe"]
+
+
+@dataclasses.dataclass(frozen=True)
+class WorkloadSpec:
+    name: str
+    frames: int          # B
+    n_cam: int           # cameras per frame
+    D: int               # depth bins
+    H: int               # feature-map rows
+    W: int               # feature-map columns
+    C: int               # feature channels
+    G: int               # BEV grid side, cells
+    cell_m: float        # BEV cell side, metres
+    r0: float            # range of depth bin 0, metres
+    span: float          # r_d = r0 + d * span / D
+    target_points: Optional[int]   # None: keep every in-grid point
+    depth_dtype: str     # "f32" | "f16"
+    feat_dtype: str      # "f32" | "f16" | "e4m3"
+    fov_deg: float = 60.0
+    yaw_step_deg: float = 60.0
+
+    @property
+    def n_img(self) -> int:
+        return self.frames * self.n_cam
+
+    @property
+    def n_frustum(self) -> int:
+        return self.n_img * self.D * self.H * self.W
+
+    @property
+    def n_cells(self) -> int:
+        return self.frames * self.G * self.G
+
+    @property
+    def n_feat_rows(self) -> int:
+        return self.n_img * self.H * self.W
+
+
+SPECS = {
+    0: WorkloadSpec("tiny", 1, 1, 8, 4, 8, 8, 16, 1.0, 1.0, 8.0, None, "f32", "f32"),
+    1: WorkloadSpec("bevdet_c80_fp16", 1, 6, 59, 16, 44, 80, 128, 0.8, 1.0, 59.0,
+                    209_000, "f16", "f16"),
+    2: WorkloadSpec("bevdet_c80_fp8", 1, 6, 59, 16, 44, 80, 128, 0.8, 1.0, 59.0,
+                    209_000, "f16", "e4m3"),
+    3: WorkloadSpec("hires_c80_fp16", 1, 6, 118, 32, 88, 80, 200, 0.5, 1.0, 59.0,
+                    None, "f16", "f16"),
+    4: WorkloadSpec("batched4_c128_fp16", 4, 6, 59, 32, 88, 128, 256, 0.4, 1.0, 59.0,
+                    1_600_000, "f16", "f16"),
+}
+
+
+def spec(k: int) -> WorkloadSpec:
+    return SPECS[k]
+
+
+@dataclasses.dataclass
+class Workload:
+    spec: WorkloadSpec
+    seed: int
+    point_cell: np.ndarray   # int32 [P]; -1 = dropped
+    depth: np.ndarray        # [n_img, D, H, W] float32 / float16
+    feat: np.ndarray         # [n_img, H, W, C] float32 / float16 / uint8 (e4m3 codes)
+    feat_scale: float        # fp8 dequant scale (1.0 for f16 / f32)
+    p_keep: float
+    in_grid: int
+
+    @property
+    def n_kept(self) -> int:
+        return int((self.point_cell >= 0).sum())
+
+
+def _frustum_cells(s: WorkloadSpec) -> np.ndarray:
+    """Cell of every frustum point in p order, before subsampling (int64)."""
+    n = np.arange(s.n_cam, dtype=np.float64)
+    d = np.arange(s.D, dtype=np.float64)
+    w = np.arange(s.W, dtype=np.float64)
+    deg = math.pi / 180.0
+    az = (s.yaw_step_deg * n[:, None] + (w[None, :] / s.W - 0.5) * s.fov_deg) * deg  # [n_cam, W]
+    r = s.r0 + d * (s.span / s.D)                                                    # [D]
+    x = r[None, :, None] * np.cos(az)[:, None, :]                                   # [n_cam, D, W]
+    y = r[None, :, None] * np.sin(az)[:, None, :]
+    half = s.G * s.cell_m / 2.0
+    ix = np.floor((x + half) / s.cell_m)
+    iy = np.floor((y + half) / s.cell_m)
+    inside = (ix >= 0) & (ix < s.G) & (iy >= 0) & (iy < s.G)
+    cell = np.where(inside, iy * s.G + ix, -1).astype(np.int64)                    # [n_cam, D, W]
+    # broadcast over rows h (the row does not move the point) and frames
+    cell = np.broadcast_to(cell[:, :, None, :], (s.n_cam, s.D, s.H, s.W))
+    cells = np.empty((s.frames, s.n_cam, s.D, s.H, s.W), dtype=np.int64)
+    for b in range(s.frames):
+        cells[b] = np.where(cell >= 0, cell + b * s.G * s.G, -1)
+    return cells.reshape(-1)
+
+
+def quantize_e4m3(x: np.ndarray):
+    """Per-tensor OCP e4m3 quantisation: codes (uint8) and fp32 scale."""
+    import torch
+    xf = np.asarray(x, dtype=np.float64)
+    absmax = float(np.abs(xf).max()) if xf.size else 0.0
+    if absmax == 0.0:
+        return np.zeros(xf.shape, np.uint8), np.float32(1.0)
+    t = torch.from_numpy(xf * (448.0 / absmax)).clamp_(-448.0, 448.0)
+    codes = t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return codes, np.float32(absmax / 448.0)
+
+
+def make_workload(k: int, seed: int = 0) -> Workload:
+    """Synthetic inputs for workload k (see SPECS), fully determined by seed."""
+    s = SPECS[k]
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((s.n_img, s.D, s.H, s.W))
+    e = np.exp(logits - logits.max(axis=1, keepdims=True))
+    probs = e / e.sum(axis=1, keepdims=True)
+    feat64 = rng.standard_normal((s.n_img, s.H, s.W, s.C))
+    u = rng.random(s.n_frustum)
+
+    cells = _frustum_cells(s)
+    in_grid = int((cells >= 0).sum())
+    p_keep = 1.0 if s.target_points is None else min(1.0, s.target_points / max(in_grid, 1))
+    keep = (cells >= 0) & (u < p_keep)
+    point_cell = np.where(keep, cells, -1).astype(np.int32)
+
+    ddt = np.float32 if s.depth_dtype == "f32" else np.float16
+    depth = probs.astype(ddt)
+    scale = np.float32(1.0)
+    if s.feat_dtype == "f32":
+        feat = feat64.astype(np.float32)
+    elif s.feat_dtype == "f16":
+        feat = feat64.astype(np.float16)
+    else:  # e4m3 codes from the fp16 features
+        feat, scale = quantize_e4m3(feat64.astype(np.float16).astype(np.float64))
+    return Workload(s, seed, point_cell, np.ascontiguousarray(depth),
+                    np.ascontiguousarray(feat), float(scale), p_keep, in_grid)
+
+
+def make_random_cells(rng: np.random.Generator, n_frustum: int, n_cells: int,
+                      p_drop: float = 0.2, hot_cells: int = 0) -> np.ndarray:
+    """Random point -> cell assignment for small edge-case geometries.
+
+    With hot_cells > 0 most points fall into that many cells, which makes
+    long intervals; otherwise cells are uniform in [0, n_cells).
+    """
+    if hot_cells > 0:
+        hot = rng.integers(0, n_cells, size=hot_cells)
+        cells = np.where(rng.random(n_frustum) < 0.8,
+                         hot[rng.integers(0, hot_cells, size=n_frustum)],
+                         rng.integers(0, n_cells, size=n_frustum))
+    else:
+        cells = rng.integers(0, n_cells, size=n_frustum)
+    cells = np.where(rng.random(n_frustum) < p_drop, -1, cells)
+    return cells.astype(np.int32)
+
+
+def describe(w: Workload) -> dict:
+    """Shape statistics of a workload (counts only; no pooling arithmetic)."""
+    kept = w.point_cell[w.point_cell >= 0]
+    counts = np.bincount(kept, minlength=w.spec.n_cells) if kept.size else np.zeros(1, np.int64)
+    occ = counts[counts > 0]
+    return {
+        "name": w.spec.name, "P": w.spec.n_frustum, "in_grid": w.in_grid,
+        "p_keep": round(w.p_keep, 6), "N": int(kept.size), "I": int(occ.size),
+        "occupied_frac": round(occ.size / w.spec.n_cells, 4),
+        "len_mean": float(occ.mean()) if occ.size else 0.0,
+        "len_median": float(np.median(occ)) if occ.size else 0.0,
+        "len_p99": float(np.percentile(occ, 99)) if occ.size else 0.0,
+        "len_max": int(occ.max()) if occ.size else 0,
+    }
