@@ -1,0 +1,148 @@
+// C ABI of the BEV-pooling library: host-side validation, then dispatch to
+// the gfx950 kernels.  Declarations and the contract live in bevpool.h.
+#include "bevpool.h"
+
+#include <climits>
+#include <cstdint>
+
+#include "bevpool_internal.h"
+
+namespace {
+
+constexpr int64_t kInt32Limit = int64_t(INT32_MAX);   // sizes must stay below 2^31
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int elem_bytes(int32_t dtype)
+{
+    switch (dtype) {
+    case BEVPOOL_F32: return 4;
+    case BEVPOOL_F16: return 2;
+    case BEVPOOL_FP8_E4M3: return 1;
+    default: return 0;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *bevpool_status_string(int status)
+{
+    switch (status) {
+    case BEVPOOL_OK: return "ok";
+    case BEVPOOL_ERR_INVALID_ARG: return "invalid argument";
+    case BEVPOOL_ERR_UNSUPPORTED: return "unsupported dtype / channel combination";
+    case BEVPOOL_ERR_OVERFLOW: return "size exceeds the INT32 index contract";
+    case BEVPOOL_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case BEVPOOL_ERR_CAPACITY: return "map arrays too small for the kept points";
+    case BEVPOOL_ERR_BAD_CELL: return "point_cell holds a value outside [-1, n_cells)";
+    case BEVPOOL_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int bevpool_version(void) { return 10000; }
+
+size_t bevpool_build_map_workspace_size(int32_t n_img, int32_t D, int32_t H, int32_t W,
+                                        int64_t n_cells)
+{
+    if (n_img <= 0 || D <= 0 || H <= 0 || W <= 0 || n_cells <= 0 || n_cells > kInt32Limit)
+        return 0;
+    const int64_t P = int64_t(n_img) * D * H * W;
+    if (P > kInt32Limit) return 0;
+    return bevpool::map_workspace_bytes(P);
+}
+
+int bevpool_build_map(const int32_t *point_cell, int32_t n_img, int32_t D, int32_t H, int32_t W,
+                      int64_t n_cells,
+                      int32_t *ranks_depth, int32_t *ranks_feat, int32_t *ranks_bev,
+                      int32_t *interval_starts, int32_t *interval_lengths, int64_t capacity,
+                      int32_t *h_n_points, int32_t *h_n_intervals,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!point_cell || !ranks_depth || !ranks_feat || !ranks_bev || !interval_starts ||
+        !interval_lengths || !h_n_points || !h_n_intervals || !workspace)
+        return BEVPOOL_ERR_INVALID_ARG;
+    if (n_img <= 0 || D <= 0 || H <= 0 || W <= 0 || n_cells <= 0 || capacity < 0)
+        return BEVPOOL_ERR_INVALID_ARG;
+    const int64_t P = int64_t(n_img) * D * H * W;
+    if (P > kInt32Limit || n_cells > kInt32Limit) return BEVPOOL_ERR_OVERFLOW;
+    if (!aligned(workspace, 256) || workspace_bytes < bevpool::map_workspace_bytes(P))
+        return BEVPOOL_ERR_WORKSPACE;
+
+    bevpool::MapParams mp{};
+    mp.point_cell = point_cell;
+    mp.P = int32_t(P);
+    mp.DHW = int32_t(int64_t(D) * H * W);
+    mp.HW = int32_t(int64_t(H) * W);
+    mp.n_cells = n_cells;
+    mp.capacity = int32_t(capacity < kInt32Limit ? capacity : kInt32Limit);
+    mp.ranks_depth = ranks_depth;
+    mp.ranks_feat = ranks_feat;
+    mp.ranks_bev = ranks_bev;
+    mp.interval_starts = interval_starts;
+    mp.interval_lengths = interval_lengths;
+    mp.workspace = workspace;
+    mp.workspace_bytes = workspace_bytes;
+
+    int32_t counts[3] = {0, 0, 0};
+    if (bevpool::run_build_map(mp, counts, stream) != hipSuccess) return BEVPOOL_ERR_HIP;
+    *h_n_points = counts[0];
+    *h_n_intervals = counts[1];
+    if (counts[2] != 0) return BEVPOOL_ERR_BAD_CELL;
+    if (counts[0] > capacity) return BEVPOOL_ERR_CAPACITY;
+    return BEVPOOL_OK;
+}
+
+int bevpool_forward(const void *depth, int32_t depth_dtype, int64_t n_depth,
+                    const void *feat, int32_t feat_dtype, int64_t n_feat_rows, int32_t C,
+                    float feat_scale,
+                    const int32_t *ranks_depth, const int32_t *ranks_feat,
+                    const int32_t *ranks_bev,
+                    const int32_t *interval_starts, const int32_t *interval_lengths,
+                    int32_t n_points, int32_t n_intervals,
+                    float *out, int64_t n_cells, hipStream_t stream)
+{
+    if (!out || n_cells <= 0 || C <= 0 || n_points < 0 || n_intervals < 0 ||
+        n_intervals > n_points)
+        return BEVPOOL_ERR_INVALID_ARG;
+    if (n_intervals > 0 && (!depth || !feat || !ranks_depth || !ranks_feat || !ranks_bev ||
+                            !interval_starts || !interval_lengths || n_depth <= 0 ||
+                            n_feat_rows <= 0))
+        return BEVPOOL_ERR_INVALID_ARG;
+
+    const int fe = elem_bytes(feat_dtype);
+    const bool pair_ok = (depth_dtype == BEVPOOL_F32 && feat_dtype == BEVPOOL_F32) ||
+                         (depth_dtype == BEVPOOL_F16 && feat_dtype == BEVPOOL_F16) ||
+                         (depth_dtype == BEVPOOL_F16 && feat_dtype == BEVPOOL_FP8_E4M3);
+    if (!pair_ok || fe == 0) return BEVPOOL_ERR_UNSUPPORTED;
+    const int64_t row_bytes = int64_t(C) * fe;
+    if (row_bytes % 16 != 0 || row_bytes > 1024) return BEVPOOL_ERR_UNSUPPORTED;
+
+    if (n_cells * C > kInt32Limit || n_feat_rows * C > kInt32Limit || n_depth > kInt32Limit)
+        return BEVPOOL_ERR_OVERFLOW;
+    if (!aligned(out, 16) || (feat && !aligned(feat, 16)) ||
+        (depth && !aligned(depth, uintptr_t(elem_bytes(depth_dtype)))))
+        return BEVPOOL_ERR_INVALID_ARG;
+
+    bevpool::FwdParams p{};
+    p.depth = depth;
+    p.feat = feat;
+    p.feat_scale = feat_scale;
+    p.C = C;
+    p.chunks = int32_t(row_bytes / 16);
+    p.ranks_depth = ranks_depth;
+    p.ranks_feat = ranks_feat;
+    p.ranks_bev = ranks_bev;
+    p.interval_starts = interval_starts;
+    p.interval_lengths = interval_lengths;
+    p.n_intervals = n_intervals;
+    p.out = out;
+    p.n_cells = int32_t(n_cells);
+    p.depth_dtype = depth_dtype;
+    p.feat_dtype = feat_dtype;
+    return bevpool::run_forward(p, stream) == hipSuccess ? BEVPOOL_OK : BEVPOOL_ERR_HIP;
+}
+
+}  // extern "C"

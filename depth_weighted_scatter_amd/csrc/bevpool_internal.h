@@ -1,0 +1,49 @@
+// Internal launch interface between the C ABI (bevpool_api.cpp) and the
+// gfx950 kernels (map_kernels.hip, forward_kernels.hip).  Not installed.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+namespace bevpool {
+
+// ---- map build -------------------------------------------------------------
+struct MapParams {
+    const int32_t *point_cell;   // [P]
+    int32_t P;                   // n_img * D * H * W (< 2^31)
+    int32_t DHW, HW;             // D*H*W and H*W, for the feature-row of point p
+    int64_t n_cells;
+    int32_t capacity;            // min(capacity, INT32_MAX) of the five output arrays
+    int32_t *ranks_depth, *ranks_feat, *ranks_bev, *interval_starts, *interval_lengths;
+    void *workspace;
+    size_t workspace_bytes;
+};
+
+// Device workspace for a frustum of P points (256-byte aligned sub-buffers).
+size_t map_workspace_bytes(int64_t P);
+
+// Enqueue the map build; on return the three counters (kept points,
+// intervals, out-of-range cells) sit at h_counts after a stream sync.
+hipError_t run_build_map(const MapParams &p, int32_t h_counts[3], hipStream_t stream);
+
+// ---- forward -----------------------------------------------------------------
+enum DType : int32_t { kF32 = 0, kF16 = 1, kE4M3 = 2 };
+
+struct FwdParams {
+    const void *depth;
+    const void *feat;            // [rows, C], 16-byte aligned
+    float feat_scale;
+    int32_t C;
+    int32_t chunks;              // 16-byte chunks per feature row (= G lanes per point)
+    const int32_t *ranks_depth, *ranks_feat, *ranks_bev, *interval_starts, *interval_lengths;
+    int32_t n_intervals;
+    float *out;                  // [n_cells, C], 16-byte aligned
+    int32_t n_cells;
+    int32_t depth_dtype, feat_dtype;
+};
+
+hipError_t run_forward(const FwdParams &p, hipStream_t stream);
+
+}  // namespace bevpool

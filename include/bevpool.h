@@ -1,0 +1,159 @@
+/*
+ * bevpool.h -- C ABI of the MI355X (gfx950) BEV-pooling library.
+ *
+ * BEV pooling lifts multi-camera image features into a top-down grid: every
+ * frustum point weights its image feature row by its depth probability and
+ * the weighted rows are summed into the BEV cell the point falls in
+ * ("Accelerating BEV Pooling on NVIDIA GPUs for Physical AI Applications",
+ * introduction and section "Remove redundant scatter traffic"):
+ *
+ *     out[ranks_bev[t], c] += depth[ranks_depth[t]] * feat[ranks_feat[t], c]
+ *
+ * The library has two calls.  bevpool_build_map turns a per-point cell index
+ * into the five-array INT32 scatter map of that section (ranks_depth,
+ * ranks_feat, ranks_bev, interval_starts, interval_lengths), once per
+ * geometry.  bevpool_forward runs the interval-owned scatter-reduce of
+ * section "Implement the interval-owned scatter-reduce": each interval of
+ * points sharing one cell has a single owner that accumulates all channels
+ * and writes the cell once; no atomics, no runtime index division.
+ *
+ * Conventions (all calls):
+ *   - Pointers without an h_ prefix are device pointers (HBM of the current
+ *     device); h_ pointers are host pointers.  The caller owns all memory;
+ *     the library allocates nothing and frees nothing.
+ *   - Every call returns a bevpool_status; no C++ exception crosses the ABI.
+ *     Arguments are validated on the host before any HIP call, so a failed
+ *     validation touches neither the GPU nor any output.
+ *   - Work is enqueued on `stream` (NULL = the null stream).
+ *   - Sizes follow the pages' INT32 map contract: point counts, cell counts
+ *     times C, and feature rows times C must stay below 2^31.
+ */
+#ifndef BEVPOOL_H
+#define BEVPOOL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bevpool_status {
+    BEVPOOL_OK = 0,
+    BEVPOOL_ERR_INVALID_ARG = -1,  /* null pointer, negative or zero size, misalignment, inconsistent counts */
+    BEVPOOL_ERR_UNSUPPORTED = -2,  /* no kernel for this (depth dtype, feat dtype, C) */
+    BEVPOOL_ERR_OVERFLOW = -3,     /* a size breaks the INT32 index contract */
+    BEVPOOL_ERR_WORKSPACE = -4,    /* workspace smaller than bevpool_build_map_workspace_size() */
+    BEVPOOL_ERR_CAPACITY = -5,     /* more kept points than the map arrays' capacity */
+    BEVPOOL_ERR_BAD_CELL = -6,     /* point_cell holds a value outside [-1, n_cells) */
+    BEVPOOL_ERR_HIP = -7           /* the HIP runtime reported an error */
+} bevpool_status;
+
+/* Element types.  FP8_E4M3 is the OCP 8-bit float E4M3 ("FN": bias 7, max
+ * 448, no infinities, NaN = S.1111.111), decoded in-kernel by gfx950's
+ * native conversion and multiplied by a per-tensor fp32 scale. */
+typedef enum bevpool_dtype {
+    BEVPOOL_F32 = 0,
+    BEVPOOL_F16 = 1,
+    BEVPOOL_FP8_E4M3 = 2
+} bevpool_dtype;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *bevpool_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int bevpool_version(void);
+
+/*
+ * Bytes of device workspace bevpool_build_map needs for a frustum of
+ * n_img*D*H*W points and n_cells cells.  Returns 0 for invalid sizes.
+ */
+size_t bevpool_build_map_workspace_size(int32_t n_img, int32_t D, int32_t H, int32_t W,
+                                        int64_t n_cells);
+
+/*
+ * bevpool_build_map -- the five-array INT32 scatter map, prepared once per
+ * geometry ahead of the forward calls (section "Implement the interval-owned
+ * scatter-reduce"; the arrays are named in section "Remove redundant scatter
+ * traffic").
+ *
+ * Input
+ *   point_cell [n_img*D*H*W] int32, device: for frustum point
+ *       p = ((img*D + d)*H + h)*W + w  its BEV cell in [0, n_cells), or -1
+ *       when the point is dropped (outside the grid, culled).  Batched frames
+ *       are folded into img and into the cell index by the caller.
+ *   n_img, D, H, W: images (frames x cameras), depth bins, feature rows and
+ *       columns; depth is laid out [n_img, D, H, W] and feat [n_img, H, W, C].
+ *   n_cells: number of BEV cells (>= 1).
+ * Output (device, capacity >= kept points each; only the first n_points /
+ * n_intervals entries are written):
+ *   ranks_depth[t] = p, ranks_feat[t] = img*H*W + h*W + w,
+ *   ranks_bev[t] = point_cell[p] for the kept points, ordered by
+ *       (cell, p) -- a total order, so the map is unique and bit-exact;
+ *   interval_starts[i], interval_lengths[i]: maximal runs of equal
+ *       ranks_bev, in increasing cell; every length >= 1.
+ *   h_n_points, h_n_intervals (host): kept point and interval counts.  They
+ *       are also reported with BEVPOOL_ERR_CAPACITY so the caller can size
+ *       the arrays and call again.
+ * workspace: device memory of at least bevpool_build_map_workspace_size()
+ *   bytes, 256-byte aligned, caller-owned; contents on entry are ignored.
+ * Blocking: returns after the map is complete (one stream synchronisation
+ *   to read the two counts back).  Not for use under stream capture.
+ * Errors: INVALID_ARG, OVERFLOW (n_img*D*H*W >= 2^31), WORKSPACE, CAPACITY,
+ *   BAD_CELL (a cell outside [-1, n_cells); the arrays are then undefined),
+ *   HIP.
+ */
+int bevpool_build_map(const int32_t *point_cell, int32_t n_img, int32_t D, int32_t H, int32_t W,
+                      int64_t n_cells,
+                      int32_t *ranks_depth, int32_t *ranks_feat, int32_t *ranks_bev,
+                      int32_t *interval_starts, int32_t *interval_lengths, int64_t capacity,
+                      int32_t *h_n_points, int32_t *h_n_intervals,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * bevpool_forward -- the depth-weighted, interval-owned scatter-reduce
+ * (section "Remove redundant scatter traffic" for the formula; section
+ * "Implement the interval-owned scatter-reduce" for the owner loop):
+ *
+ *   out[cell, c] = sum over the points t of the interval whose cell it is of
+ *                  depth[ranks_depth[t]] * feat[ranks_feat[t], c] (* feat_scale)
+ *
+ * accumulated in fp32 registers and written once; cells without an interval
+ * are written as 0.  Every element of out is written, so out needs no
+ * clearing.
+ *
+ *   depth [n_depth] (device): depth probabilities, read flat through
+ *       ranks_depth; depth_dtype BEVPOOL_F32 or BEVPOOL_F16.
+ *   feat [n_feat_rows, C] (device, 16-byte aligned): channel-last feature
+ *       rows; feat_dtype BEVPOOL_F32, BEVPOOL_F16 or BEVPOOL_FP8_E4M3.
+ *   feat_scale: dequantisation scale applied to FP8_E4M3 features (ignored
+ *       for the other types).
+ *   Supported pairs: (F32 depth, F32 feat); (F16 depth, F16 feat);
+ *       (F16 depth, FP8_E4M3 feat).  One feature row must be a multiple of
+ *       16 bytes and at most 1024 bytes: C % 4 == 0 and C <= 256 for F32,
+ *       C % 8 == 0 and C <= 512 for F16, C % 16 == 0 and C <= 1024 for
+ *       FP8_E4M3.  Anything else returns BEVPOOL_ERR_UNSUPPORTED.
+ *   ranks_*, interval_*: a map as produced by bevpool_build_map for this
+ *       geometry (n_points, n_intervals entries).  The kernel trusts the map:
+ *       indices outside depth / feat / out are undefined behaviour.
+ *   out [n_cells, C] fp32 (device, 16-byte aligned), overwritten.
+ * Asynchronous: enqueues on `stream` and returns; never synchronises or
+ * allocates, so it may be captured into a HIP graph.
+ * Errors: INVALID_ARG, UNSUPPORTED, OVERFLOW, HIP (launch failure).
+ */
+int bevpool_forward(const void *depth, int32_t depth_dtype, int64_t n_depth,
+                    const void *feat, int32_t feat_dtype, int64_t n_feat_rows, int32_t C,
+                    float feat_scale,
+                    const int32_t *ranks_depth, const int32_t *ranks_feat,
+                    const int32_t *ranks_bev,
+                    const int32_t *interval_starts, const int32_t *interval_lengths,
+                    int32_t n_points, int32_t n_intervals,
+                    float *out, int64_t n_cells, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BEVPOOL_H */

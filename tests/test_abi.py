@@ -1,0 +1,113 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/bevpool.h declares, and rejects bad arguments on the host before any
+HIP call (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import depth_weighted_scatter_amd as dws
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bevpool.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bevpool_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dws.library_path()):
+        import depth_weighted_scatter_amd.build as b
+        b.build()
+    return dws._load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("bevpool_build_map", "bevpool_forward", "bevpool_build_map_workspace_size",
+                     "bevpool_status_string"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    handle = ctypes.CDLL(dws.library_path())
+    for name in declared_functions():
+        assert hasattr(handle, name), f"{name} declared in bevpool.h but not exported"
+
+
+def test_status_strings(lib):
+    for code in range(0, -8, -1):
+        s = dws.bevpool_status_string(code)
+        assert s and s != "unknown status"
+    assert dws.bevpool_status_string(-99) == "unknown status"
+    assert dws.bevpool_version() >= 10000
+
+
+def test_workspace_size(lib):
+    assert dws.bevpool_build_map_workspace_size(6, 59, 16, 44, 128 * 128) > 5 * 249216 * 4
+    assert dws.bevpool_build_map_workspace_size(0, 1, 1, 1, 10) == 0
+    assert dws.bevpool_build_map_workspace_size(1, 1, 1, 1, 0) == 0
+    assert dws.bevpool_build_map_workspace_size(1 << 15, 1 << 15, 4, 1, 10) == 0  # P >= 2^31
+
+
+FAKE = 1 << 40          # never dereferenced: validation fails first
+
+
+def _fwd(lib, **kw):
+    a = dict(depth=FAKE, ddt=dws.F16, n_depth=100, feat=FAKE, fdt=dws.F16, rows=10, C=80,
+             scale=1.0, rd=FAKE, rf=FAKE, rb=FAKE, st=FAKE, ln=FAKE, n_points=5, n_iv=2,
+             out=FAKE, n_cells=16, stream=None)
+    a.update(kw)
+    return lib.bevpool_forward(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=None), -1),
+    (dict(depth=None), -1),
+    (dict(rd=None), -1),
+    (dict(C=0), -1),
+    (dict(n_cells=0), -1),
+    (dict(n_iv=6), -1),                         # more intervals than points
+    (dict(n_points=-1), -1),
+    (dict(ddt=dws.F32), -2),                    # f32 depth with f16 feat
+    (dict(fdt=7), -2),
+    (dict(C=12), -2),                           # 24-byte rows are not 16-byte chunks
+    (dict(C=1024), -2),                         # 2 KB rows
+    (dict(fdt=dws.FP8_E4M3, C=8), -2),          # 8-byte fp8 rows
+    (dict(n_cells=1 << 26, C=64), -3),          # n_cells * C >= 2^31
+    (dict(rows=1 << 26, C=64), -3),
+    (dict(out=FAKE + 4), -1),                   # misaligned output
+    (dict(feat=FAKE + 8), -1),                  # misaligned features
+])
+def test_forward_rejects(lib, kw, code):
+    assert _fwd(lib, **kw) == code
+
+
+def _map(lib, **kw):
+    n_pts, n_iv = ctypes.c_int32(), ctypes.c_int32()
+    a = dict(pc=FAKE, n_img=1, D=2, H=2, W=2, n_cells=4, rd=FAKE, rf=FAKE, rb=FAKE, st=FAKE,
+             ln=FAKE, cap=8, hn=ctypes.byref(n_pts), hi=ctypes.byref(n_iv), ws=FAKE,
+             ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return lib.bevpool_build_map(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pc=None), -1),
+    (dict(ln=None), -1),
+    (dict(ws=None), -1),
+    (dict(D=0), -1),
+    (dict(n_cells=0), -1),
+    (dict(cap=-1), -1),
+    (dict(n_img=1 << 16, D=1 << 16), -3),        # P >= 2^31
+    (dict(n_cells=1 << 31), -3),
+    (dict(ws_bytes=16), -4),
+    (dict(ws=FAKE + 64), -4),                    # workspace not 256-byte aligned
+])
+def test_build_map_rejects(lib, kw, code):
+    assert _map(lib, **kw) == code

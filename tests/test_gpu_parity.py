@@ -1,0 +1,260 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+The map must match bit for bit; the pooled output must be within the scaled
+error bound (1e-3 for fp32/fp16 features, 2e-2 for e4m3, see gpu_util.TOL),
+with empty cells exactly zero.  Inputs are the seeded synthetic workloads
+plus small geometries that span several tiles with ragged tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import depth_weighted_scatter_amd as dws
+import oracle
+import workloads as W
+from gpu_util import (MAP_KEYS, assert_maps_equal, check_forward, gpu_forward, gpu_map,
+                      map_from_numpy, map_to_numpy, oracle_reference, say, to_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    oracle.build(force=False)
+    dws._load()          # raises if the HIP library is not built
+
+
+def _workload_case(k):
+    wl = W.make_workload(k)
+    s = wl.spec
+    say(f"[workload {k} {s.name}] P={s.n_frustum} n_cells={s.n_cells} C={s.C} {s.feat_dtype}")
+    ref = oracle.build_map(wl.point_cell, s.n_img, s.D, s.H, s.W, s.n_cells)
+    return wl, s, ref
+
+
+# ------------------------------------------------------------------ maps
+@pytest.mark.parametrize("k", [0, 1, 2, 3, 4])
+def test_map_bit_exact_on_workloads(k):
+    wl, s, ref = _workload_case(k)
+    m = gpu_map(wl.point_cell, s.n_img, s.D, s.H, s.W, s.n_cells)
+    assert_maps_equal(map_to_numpy(m), ref, f"workload {k}")
+
+
+def _random_geometry(rng, P_max):
+    n_img = int(rng.integers(1, 4))
+    D = int(rng.integers(1, 9))
+    H = int(rng.integers(1, 9))
+    Wd = int(rng.integers(1, max(2, P_max // (n_img * D * H))))
+    return n_img, D, H, Wd
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_map_bit_exact_random(seed):
+    rng = np.random.default_rng(100 + seed)
+    n_img, D, H, Wd = _random_geometry(rng, 40000)
+    P = n_img * D * H * Wd
+    n_cells = int(rng.choice([1, 2, 7, 300, 5000, 70000, 1 << 20, (1 << 31) - 1]))
+    pc = W.make_random_cells(rng, P, min(n_cells, 1 << 30), p_drop=float(rng.choice([0, .3, .95])),
+                             hot_cells=int(rng.choice([0, 1, 3])))
+    say(f"[random map seed={seed}] P={P} geometry={(n_img, D, H, Wd)} n_cells={n_cells}")
+    ref = oracle.build_map(pc, n_img, D, H, Wd, n_cells)
+    got = map_to_numpy(gpu_map(pc, n_img, D, H, Wd, n_cells))
+    assert_maps_equal(got, ref, f"seed {seed}")
+
+
+@pytest.mark.parametrize("case", ["all_dropped", "one_point", "one_cell", "single_cell_grid",
+                                  "tile_minus_1", "tile_plus_1", "last_cell_only"])
+def test_map_edge_cases(case):
+    rng = np.random.default_rng(7)
+    n_img, D, H, Wd, n_cells = 1, 1, 1, 5000, 64
+    if case == "tile_minus_1":
+        Wd = 2 * 2048 - 1
+    elif case == "tile_plus_1":
+        Wd = 2 * 2048 + 1
+    P = n_img * D * H * Wd
+    pc = W.make_random_cells(rng, P, n_cells, p_drop=0.2)
+    if case == "all_dropped":
+        pc[:] = -1
+    elif case == "one_point":
+        pc[:] = -1
+        pc[P // 2] = 17
+    elif case == "one_cell":
+        pc[pc >= 0] = 31
+    elif case == "single_cell_grid":
+        n_cells = 1
+        pc[pc >= 0] = 0
+    elif case == "last_cell_only":
+        pc[::3] = n_cells - 1
+    say(f"[map edge {case}] P={P} n_cells={n_cells}")
+    ref = oracle.build_map(pc, n_img, D, H, Wd, n_cells)
+    got = map_to_numpy(gpu_map(pc, n_img, D, H, Wd, n_cells))
+    assert_maps_equal(got, ref, case)
+
+
+def test_map_rejects_bad_cell_and_small_capacity():
+    pc = np.array([0, 3, -1, 2, 1, 4], np.int32)
+    say("[map errors] bad cell")
+    with pytest.raises(dws.BevPoolError) as ei:
+        gpu_map(pc, 1, 1, 1, 6, 4)
+    assert ei.value.status == -6
+    pc = np.array([0, 3, -1, 2, 1, 2], np.int32)
+    say("[map errors] capacity")
+    with pytest.raises(dws.BevPoolError) as ei:
+        gpu_map(pc, 1, 1, 1, 6, 4, capacity=3)
+    assert ei.value.status == -5
+    m = gpu_map(pc, 1, 1, 1, 6, 4, capacity=5)
+    assert m.n_points == 5 and m.n_intervals == 4
+
+
+# --------------------------------------------------------------- forward
+@pytest.mark.parametrize("k", [0, 1, 2, 3, 4])
+def test_forward_on_workloads(k):
+    wl, s, ref = _workload_case(k)
+    m = gpu_map(wl.point_cell, s.n_img, s.D, s.H, s.W, s.n_cells)
+    assert_maps_equal(map_to_numpy(m), ref, f"workload {k}")
+    out_ref, out_abs = oracle_reference(wl.depth, wl.feat, s.feat_dtype, wl.feat_scale, s.C, ref,
+                                        s.n_cells)
+    say(f"  forward workload {k}")
+    got = gpu_forward(wl.depth, wl.feat, wl.feat_scale, m, s.n_cells, s.C)
+    check_forward(got, out_ref, out_abs, s.feat_dtype, ref["ranks_bev"], f"workload {k}")
+    again = gpu_forward(wl.depth, wl.feat, wl.feat_scale, m, s.n_cells, s.C)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32)), "not deterministic"
+
+
+def _make_inputs(rng, n_img, D, H, Wd, C, feat_dtype):
+    depth = rng.random((n_img, D, H, Wd))
+    depth /= depth.sum(axis=1, keepdims=True)
+    feat = rng.standard_normal((n_img, H, Wd, C))
+    scale = 1.0
+    if feat_dtype == "f32":
+        return depth.astype(np.float32), feat.astype(np.float32), scale
+    if feat_dtype == "f16":
+        return depth.astype(np.float16), feat.astype(np.float16), scale
+    q, scale = W.quantize_e4m3(feat.astype(np.float16))
+    return depth.astype(np.float16), q, float(scale)
+
+
+CHANNEL_CASES = [("f32", 4), ("f32", 8), ("f32", 12), ("f32", 80), ("f32", 128), ("f32", 256),
+                 ("f16", 8), ("f16", 24), ("f16", 64), ("f16", 80), ("f16", 96), ("f16", 128),
+                 ("f16", 256), ("f16", 512),
+                 ("e4m3", 16), ("e4m3", 48), ("e4m3", 80), ("e4m3", 128), ("e4m3", 256),
+                 ("e4m3", 1024)]
+
+
+@pytest.mark.parametrize("feat_dtype,C", CHANNEL_CASES, ids=[f"{a}-C{b}" for a, b in CHANNEL_CASES])
+def test_forward_channel_widths(feat_dtype, C):
+    rng = np.random.default_rng(C * 7 + len(feat_dtype))
+    n_img, D, H, Wd, n_cells = 2, 6, 5, 37, 97
+    P = n_img * D * H * Wd
+    pc = W.make_random_cells(rng, P, n_cells, p_drop=0.3, hot_cells=2)
+    depth, feat, scale = _make_inputs(rng, n_img, D, H, Wd, C, feat_dtype)
+    say(f"[forward C={C} {feat_dtype}] P={P} n_cells={n_cells}")
+    ref = oracle.build_map(pc, n_img, D, H, Wd, n_cells)
+    m = gpu_map(pc, n_img, D, H, Wd, n_cells)
+    assert_maps_equal(map_to_numpy(m), ref, "map")
+    out_ref, out_abs = oracle_reference(depth, feat, feat_dtype, scale, C, ref, n_cells)
+    got = gpu_forward(depth, feat, scale, m, n_cells, C)
+    check_forward(got, out_ref, out_abs, feat_dtype, ref["ranks_bev"], f"C={C} {feat_dtype}")
+
+
+@pytest.mark.parametrize("feat_dtype,C", [("f32", 8), ("f16", 80), ("e4m3", 80), ("f16", 128)])
+def test_forward_length_one_intervals_bit_exact(feat_dtype, C):
+    """One point per cell: out = d * f (* scale) with a single rounding, so
+    the GPU must equal the oracle rounded to fp32 exactly."""
+    rng = np.random.default_rng(11)
+    n_img, D, H, Wd = 1, 4, 8, 16
+    P = n_img * D * H * Wd
+    n_cells = P + 13
+    pc = rng.permutation(n_cells)[:P].astype(np.int32)
+    pc[rng.random(P) < 0.25] = -1
+    depth, feat, scale = _make_inputs(rng, n_img, D, H, Wd, C, feat_dtype)
+    say(f"[length-1 {feat_dtype} C={C}]")
+    ref = oracle.build_map(pc, n_img, D, H, Wd, n_cells)
+    assert (ref["interval_lengths"] == 1).all()
+    out_ref = oracle.forward(depth, feat, feat_dtype, scale, C, ref, n_cells)
+    got = gpu_forward(depth, feat, scale, map_from_numpy(ref), n_cells, C)
+    assert np.array_equal(got, out_ref.astype(np.float32))
+
+
+def test_forward_e4m3_every_code():
+    """All 254 finite e4m3 codes through the kernel's native fp8 decode."""
+    C = 16
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    feat = np.zeros((16, 16, C), np.uint8)
+    feat.reshape(-1)[:codes.size] = codes
+    n_img, D, H, Wd = 1, 1, 16, 16                # 256 points; row(p) = p
+    P = 256
+    pc = np.arange(P, dtype=np.int32)              # one point per cell
+    depth = np.ones((n_img, D, H, Wd), np.float16)
+    scale = 0.5
+    say("[e4m3 every code]")
+    ref = oracle.build_map(pc, n_img, D, H, Wd, P)
+    out_ref = oracle.forward(depth, feat, "e4m3", scale, C, ref, P)
+    got = gpu_forward(depth, feat, scale, map_from_numpy(ref), P, C)
+    assert np.array_equal(got, out_ref.astype(np.float32))
+    dec = oracle.decode_e4m3(codes) * scale
+    assert np.array_equal(got.reshape(-1)[:codes.size], dec.astype(np.float32))
+
+
+@pytest.mark.parametrize("case", ["no_points", "one_long_interval", "long_and_short",
+                                  "first_and_last_cell", "single_cell_grid"])
+def test_forward_edge_cases(case):
+    rng = np.random.default_rng(5)
+    n_img, D, H, Wd, C, n_cells = 1, 8, 16, 40, 80, 300
+    P = n_img * D * H * Wd
+    pc = W.make_random_cells(rng, P, n_cells, p_drop=0.5)
+    if case == "no_points":
+        pc[:] = -1
+    elif case == "one_long_interval":
+        pc[pc >= 0] = 123                           # ~2500 points: many 64-point batches
+    elif case == "long_and_short":
+        pc[::2] = 7
+    elif case == "first_and_last_cell":
+        pc = np.where(pc >= 0, np.where(pc % 2 == 0, 0, n_cells - 1), -1).astype(np.int32)
+    elif case == "single_cell_grid":
+        n_cells = 1
+        pc[pc >= 0] = 0
+    depth, feat, scale = _make_inputs(rng, n_img, D, H, Wd, C, "f16")
+    say(f"[forward edge {case}]")
+    ref = oracle.build_map(pc, n_img, D, H, Wd, n_cells)
+    m = gpu_map(pc, n_img, D, H, Wd, n_cells)
+    assert_maps_equal(map_to_numpy(m), ref, case)
+    out_ref, out_abs = oracle_reference(depth, feat, "f16", scale, C, ref, n_cells)
+    got = gpu_forward(depth, feat, scale, m, n_cells, C)
+    check_forward(got, out_ref, out_abs, "f16", ref["ranks_bev"], case)
+    if case == "no_points":
+        assert (got == 0).all()
+
+
+def test_forward_graph_replay_matches_eager():
+    """Captured forward calls replayed several times, with eager work and
+    synchronisations in between; every replay must equal the eager result."""
+    wl, s, ref = _workload_case(1)
+    m = gpu_map(wl.point_cell, s.n_img, s.D, s.H, s.W, s.n_cells)
+    depth, feat = to_gpu(wl.depth), to_gpu(wl.feat)
+    eager = torch.empty((s.n_cells, s.C), dtype=torch.float32, device="cuda")
+    dws.bevpool_forward(depth, feat, m, s.n_cells, out=eager)
+    torch.cuda.synchronize()
+    outs = [torch.full_like(eager, float("nan")) for _ in range(3)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):      # warm the binding on a side stream first
+        dws.bevpool_forward(depth, feat, m, s.n_cells, out=outs[0])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for o in outs:
+            dws.bevpool_forward(depth, feat, m, s.n_cells, out=o)
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        _ = (depth.float() * 2).sum()               # unrelated eager work
+        torch.cuda.synchronize()
+        say(f"  graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for o in outs:
+            assert torch.equal(o, eager), f"replay {rep} differs from eager"
