@@ -53,22 +53,19 @@ template <> struct Chunk<kF32> { static constexpr int kElems = 4; };
 template <> struct Chunk<kF16> { static constexpr int kElems = 8; };
 template <> struct Chunk<kE4M3> { static constexpr int kElems = 16; };
 
-template <int DT> __device__ inline float load_depth(const void *depth, int i);
-template <> __device__ inline float load_depth<kF32>(const void *depth, int i)
-{
-    return static_cast<const float *>(depth)[i];
-}
-template <> __device__ inline float load_depth<kF16>(const void *depth, int i)
-{
-    return static_cast<float>(static_cast<const _Float16 *>(depth)[i]);
-}
+// Depth values are gathered in their storage type and widened at first use,
+// so the gather can stay in flight while other work issues.
+template <int DT> struct DepthT;
+template <> struct DepthT<kF32> { using type = float; };
+template <> struct DepthT<kF16> { using type = _Float16; };
 
 // acc[e] += d * value(e) for the elements of one 16-byte chunk.
 template <int FT> __device__ inline void accumulate(float *acc, float d, u32x4 v);
 template <> __device__ inline void accumulate<kF32>(float *acc, float d, u32x4 v)
 {
+    const f32x4 f = __builtin_bit_cast(f32x4, v);   // whole-vector cast
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(d, __builtin_bit_cast(float, v[e]), acc[e]);
+    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(d, f[e], acc[e]);
 }
 template <> __device__ inline void accumulate<kF16>(float *acc, float d, u32x4 v)
 {
@@ -107,14 +104,28 @@ __device__ inline void zero_cells(float *out, int C, int cell_lo, int cell_hi, i
     for (int q = q0 + lane; q < q1; q += kWave) __builtin_nontemporal_store(z, o + q);
 }
 
+// Lane i reads the map indices of point t0 + min(i, n - 1), 1 <= n <= 64:
+// lanes past the batch repeat its last point, so every address derived from
+// them stays in bounds and no lane needs an exec-masked branch.
+__device__ inline void load_indices(const FwdParams &p, int t0, int n, int lane, int &row,
+                                    int &didx)
+{
+    const int t = t0 + min(lane, n - 1);
+    row = __builtin_nontemporal_load(p.ranks_feat + t);
+    didx = __builtin_nontemporal_load(p.ranks_depth + t);
+}
+
 // G_CT > 0: lanes per point fixed at compile time; G_CT == 0: p.chunks.
 template <int DT, int FT, int G_CT>
 __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
 {
     constexpr int E = Chunk<FT>::kElems;
-    constexpr int PPW_CT = G_CT > 0 ? kWave / G_CT : 0;
-    // sub-iterations whose loads are issued together (about 24 points)
-    constexpr int U = G_CT > 0 ? (PPW_CT >= 24 ? 1 : (24 / PPW_CT > 8 ? 8 : 24 / PPW_CT)) : 4;
+    constexpr int PPW_CT = G_CT > 0 ? kWave / G_CT : 1;
+    // sub-iterations (PPW rows each) whose feature loads are in flight together:
+    // a whole 64-point batch when it fits in 16 loads of 16 bytes per lane
+    constexpr int NS_FULL = (kWave + PPW_CT - 1) / PPW_CT;
+    constexpr int SUB = G_CT > 0 ? (NS_FULL > 16 ? 16 : NS_FULL) : 4;
+    constexpr int CH = 4;   // sub-iterations per branch-free chunk
     __shared__ __attribute__((aligned(16))) float red[kWavesPerBlock][kWave * E];
 
     const int G = G_CT > 0 ? G_CT : p.chunks;
@@ -127,8 +138,6 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
     const int C = p.C;
     const int start = p.interval_starts[iv];
     const int len = p.interval_lengths[iv];
-    const int bev = p.ranks_bev[start];
-    const int prev_bev = iv > 0 ? p.ranks_bev[start - 1] : -1;
 
     const int g = lane / G;
     const int k = lane - g * G;
@@ -139,32 +148,66 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
 
-    for (int base = 0; base < len; base += kWave) {
-        const int nb = min(kWave, len - base);
-        // one coalesced read of up to 64 points' indices; depth gathered once per point
-        int my_chunk = 0;
-        float my_d = 0.f;
-        if (lane < nb) {
-            const int t = start + base + lane;
-            my_chunk = __builtin_nontemporal_load(p.ranks_feat + t) * G;
-            my_d = load_depth<DT>(p.depth, __builtin_nontemporal_load(p.ranks_depth + t));
-        }
-        for (int s0 = 0; s0 < nb; s0 += U * PPW) {
-            u32x4 v[U];
-            float dv[U];
+    using DRaw = typename DepthT<DT>::type;
+    const DRaw *depth = static_cast<const DRaw *>(p.depth);
+
+    // Points are walked in batches of 64.  For batch b the feature rows are
+    // requested first (they need only the row indices), then the batch's
+    // depth values (their indices are already here), then the indices of
+    // batch b+1; accumulation waits for all of it.  Nothing is in flight
+    // across the loop edge, so a batch costs one memory round trip once its
+    // indices are known, and the first batch two.
+    const int n_batches = (len + kWave - 1) / kWave;
+    int row0, didx0;
+    load_indices(p, start, min(kWave, len), lane, row0, didx0);
+
+    for (int b = 0; b < n_batches; ++b) {
+        const int nb = min(kWave, len - b * kWave);
+        const bool more = b + 1 < n_batches;                  // wave-uniform
+        const int my_chunk = row0 * G;
+        DRaw draw = DRaw(0);
+        int row1 = 0, didx1 = 0;
+        for (int s0 = 0; s0 < nb; s0 += SUB * PPW) {
+            u32x4 v[SUB];
+            // Chunks of CH sub-iterations are branch-free: every lane loads an
+            // in-bounds row (lanes past the batch repeat its last point, k < G),
+            // slots without a point are zeroed by select at first use, so the
+            // shuffles and loads of a chunk issue back to back.  Only the chunk
+            // guard, which is wave-uniform, branches.
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int j = s0 + u * PPW + g;
-                const int row = __shfl(my_chunk, j & (kWave - 1));
-                const float d = __shfl(my_d, j & (kWave - 1));
-                const bool ok = slot_ok && j < nb;
-                dv[u] = ok ? d : 0.f;
-                v[u] = u32x4{0u, 0u, 0u, 0u};
-                if (ok) v[u] = feat[row + k];
+            for (int c = 0; c < SUB; c += CH) {
+                if (s0 + c * PPW < nb) {
+#pragma unroll
+                    for (int u = c; u < c + CH && u < SUB; ++u) {
+                        const int j = s0 + u * PPW + g;
+                        const int row = __shfl(my_chunk, j & (kWave - 1));
+                        v[u] = feat[row + k];
+                    }
+                }
             }
+            if (s0 == 0) {
+                draw = depth[didx0];
+                if (more)
+                    load_indices(p, start + (b + 1) * kWave, min(kWave, len - (b + 1) * kWave),
+                                 lane, row1, didx1);
+            }
+            // depth values and the validity selects are first needed here
+            const float my_d = static_cast<float>(draw);
 #pragma unroll
-            for (int u = 0; u < U; ++u) accumulate<FT>(acc, dv[u], v[u]);
+            for (int c = 0; c < SUB; c += CH) {
+                if (s0 + c * PPW < nb) {
+#pragma unroll
+                    for (int u = c; u < c + CH && u < SUB; ++u) {
+                        const int j = s0 + u * PPW + g;
+                        const float d = __shfl(my_d, j & (kWave - 1));
+                        const bool ok = slot_ok && j < nb;
+                        accumulate<FT>(acc, ok ? d : 0.f, ok ? v[u] : u32x4{0u, 0u, 0u, 0u});
+                    }
+                }
+            }
         }
+        row0 = row1;
+        didx0 = didx1;
     }
     if (FT == kE4M3) {
 #pragma unroll
@@ -182,6 +225,8 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+    const int bev = p.ranks_bev[start];
+    const int prev_bev = iv > 0 ? p.ranks_bev[start - 1] : -1;
     f32x4 *o = reinterpret_cast<f32x4 *>(p.out);
     const int C4 = C / 4;
     for (int q = lane; q < C4; q += kWave) {
