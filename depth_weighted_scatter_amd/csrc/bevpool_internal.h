@@ -39,6 +39,7 @@ struct FwdParams {
     int32_t chunks;              // 16-byte chunks per feature row (= G lanes per point)
     const int32_t *ranks_depth, *ranks_feat, *ranks_bev, *interval_starts, *interval_lengths;
     int32_t n_intervals;
+    int32_t n_long_blocks;       // blocks in the long-interval role (set by run_forward)
     float *out;                  // [n_cells, C], 16-byte aligned
     int32_t n_cells;
     int32_t depth_dtype, feat_dtype;

@@ -10,26 +10,39 @@
 // arrays carry explicit indices so nothing is divided at run time.
 //
 // CDNA4 mapping (our design, not the pages'):
-//   * One 64-lane wavefront owns one interval.  A feature row is split into
-//     G = rowbytes/16 chunks of 16 bytes; lane (g, k) = g*G + k loads chunk k
-//     of point slot g, so one wave instruction gathers PPW = 64/G rows with
-//     dwordx4 loads (C=80 fp16: G=10, six rows per instruction).
-//   * Map indices of up to 64 points are read with one coalesced load per
-//     array (non-temporal: they are read once), the depth value of each point
-//     is gathered once by the lane that read its index, and both are handed
-//     to the lanes of slot g with ds_bpermute.
-//   * fp16 features feed v_fma_mix_f32 directly; e4m3 features go through the
-//     native OCP-fp8 v_cvt_pk_f32_fp8; accumulation is fp32 in registers.
-//   * The PPW partial rows are summed through a per-wave LDS slice, and the
-//     owner writes the cell with non-temporal 16-byte stores so the output
-//     stream does not evict feature rows from L2 (the pages' cache-streaming
-//     output stores, section "Map the algorithm to hardware").
+//   * A feature row is split into G = rowbytes/16 chunks of 16 bytes; lane
+//     (g, k) = g*G + k loads chunk k of point slot g, so one wave
+//     instruction gathers PPW = 64/G rows with dwordx4 loads (C=80 fp16:
+//     G=10, six rows per instruction).  Row loads use a scalar base and a
+//     32-bit per-lane byte offset.
+//   * The map indices of up to 64 points come in with one coalesced load per
+//     array; each point's depth is gathered once by the lane that read its
+//     index and handed to the lanes of its slot with ds_bpermute.
+//   * fp16 features feed v_fma_mix_f32; e4m3 features go through gfx950's
+//     OCP-fp8 v_cvt_pk_f32_fp8; accumulation is fp32 in registers.
+//   * The PPW slot accumulators of a wave are folded through LDS and the cell
+//     is written with non-temporal 16-byte stores, so the output stream does
+//     not evict feature rows from L2 (the pages' cache-streaming stores,
+//     section "Map the algorithm to hardware").
 //   * Cells without points: intervals come in increasing cell order, so the
 //     owner of interval i also zeroes the cells between the previous
-//     interval's cell and its own, and the last owner zeroes the tail.  Every
+//     interval's cell and its own, and the last owner zeroes the tail; every
 //     output element is stored exactly once and no memset is needed.
-//   * Blocks are renumbered so each of the 8 XCDs (own L2 each) takes a
-//     contiguous run of intervals, i.e. a spatially coherent patch of cells.
+//
+// The kernel is latency-bound (a 209K-point frame moves ~10 MB through HBM),
+// so the launch is shaped for memory-level parallelism:
+//   * Short intervals (<= 64 points, ~98% of them) get one wave each, in
+//     blocks of four, with a small register budget so eight waves fit per
+//     SIMD.
+//   * Long intervals (cells near the cameras, clustered in cell order) would
+//     each pin one wave for many round trips.  The first n_long_blocks blocks
+//     therefore own them instead: block b takes the long intervals b, b+n,
+//     b+2n, ... (so a cluster spreads over many blocks), its four waves split
+//     each one's points, and the partial rows are summed through LDS in wave
+//     order before the single write.  These blocks are dispatched first, so
+//     the long intervals overlap the short ones.
+//   Blocks go out in interval order (no XCD remapping): giving each XCD a
+//   contiguous range of cells piled the long intervals onto one or two XCDs.
 #include <hip/hip_runtime.h>
 
 #include "bevpool_internal.h"
@@ -45,7 +58,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = kWave * kWavesPerBlock;
-constexpr int kXcds = 8;
+constexpr int kShortMax = 64;   // longest interval a single wave owns
 
 // Element types of one 16-byte chunk.
 template <int FT> struct Chunk;
@@ -53,8 +66,7 @@ template <> struct Chunk<kF32> { static constexpr int kElems = 4; };
 template <> struct Chunk<kF16> { static constexpr int kElems = 8; };
 template <> struct Chunk<kE4M3> { static constexpr int kElems = 16; };
 
-// Depth values are gathered in their storage type and widened at first use,
-// so the gather can stay in flight while other work issues.
+// Depth values are gathered in their storage type and widened at first use.
 template <int DT> struct DepthT;
 template <> struct DepthT<kF32> { using type = float; };
 template <> struct DepthT<kF16> { using type = _Float16; };
@@ -86,22 +98,15 @@ template <> __device__ inline void accumulate<kE4M3>(float *acc, float d, u32x4 
     }
 }
 
-// Block index -> work index such that XCD x (blocks x, x+8, x+16, ... under
-// round-robin dispatch) receives one contiguous range of work indices.
-__device__ inline int xcd_contiguous_block(int bid, int nblocks)
-{
-    const int q = nblocks / kXcds, r = nblocks % kXcds;
-    const int x = bid % kXcds, slot = bid / kXcds;
-    return x * q + min(x, r) + slot;
-}
-
-__device__ inline void zero_cells(float *out, int C, int cell_lo, int cell_hi, int lane)
+// Zeroes cells [cell_lo, cell_hi) of out with non-temporal stores; `lane`
+// and `lanes` give this thread's position among the cooperating threads.
+__device__ inline void zero_cells(float *out, int C, int cell_lo, int cell_hi, int lane, int lanes)
 {
     if (cell_hi <= cell_lo) return;
     f32x4 *o = reinterpret_cast<f32x4 *>(out);
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     const int q0 = cell_lo * (C / 4), q1 = cell_hi * (C / 4);
-    for (int q = q0 + lane; q < q1; q += kWave) __builtin_nontemporal_store(z, o + q);
+    for (int q = q0 + lane; q < q1; q += lanes) __builtin_nontemporal_store(z, o + q);
 }
 
 // Lane i reads the map indices of point t0 + min(i, n - 1), 1 <= n <= 64:
@@ -115,128 +120,178 @@ __device__ inline void load_indices(const FwdParams &p, int t0, int n, int lane,
     didx = __builtin_nontemporal_load(p.ranks_depth + t);
 }
 
-// G_CT > 0: lanes per point fixed at compile time; G_CT == 0: p.chunks.
-template <int DT, int FT, int G_CT>
-__global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
+// Lane geometry of a wave: lane (g, k) = g*G + k holds chunk k of slot g.
+struct Slots {
+    int G, PPW, g, k, lane;
+    bool ok;   // g < PPW (the last 64 mod G lanes idle)
+};
+
+// Accumulates points [t0, t0 + n) (n >= 1) into this lane's acc, in batches
+// of 64 points.  For each batch the feature rows go out first (they need
+// only the row indices), then the batch's depth values, then the indices of
+// the next batch; accumulation waits for all of it.  Rows of a batch are
+// requested SUB sub-iterations (SUB*PPW points) at a time.
+template <int DT, int FT, int SUB>
+__device__ inline void accumulate_points(const FwdParams &p, int t0, int n, const Slots &s,
+                                         float *acc)
 {
-    constexpr int E = Chunk<FT>::kElems;
-    constexpr int PPW_CT = G_CT > 0 ? kWave / G_CT : 1;
-    // sub-iterations (PPW rows each) whose feature loads are in flight together:
-    // a whole 64-point batch when it fits in 16 loads of 16 bytes per lane
-    constexpr int NS_FULL = (kWave + PPW_CT - 1) / PPW_CT;
-    constexpr int SUB = G_CT > 0 ? (NS_FULL > 16 ? 16 : NS_FULL) : 4;
-    constexpr int CH = 4;   // sub-iterations per branch-free chunk
-    __shared__ __attribute__((aligned(16))) float red[kWavesPerBlock][kWave * E];
-
-    const int G = G_CT > 0 ? G_CT : p.chunks;
-    const int PPW = G_CT > 0 ? PPW_CT : kWave / G;
-    const int lane = __lane_id();
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int iv = xcd_contiguous_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
-    if (iv >= p.n_intervals) return;
-
-    const int C = p.C;
-    const int start = p.interval_starts[iv];
-    const int len = p.interval_lengths[iv];
-
-    const int g = lane / G;
-    const int k = lane - g * G;
-    const bool slot_ok = g < PPW;
-    const u32x4 *feat = static_cast<const u32x4 *>(p.feat);
-
-    float acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
-
     using DRaw = typename DepthT<DT>::type;
     const DRaw *depth = static_cast<const DRaw *>(p.depth);
-
-    // Points are walked in batches of 64.  For batch b the feature rows are
-    // requested first (they need only the row indices), then the batch's
-    // depth values (their indices are already here), then the indices of
-    // batch b+1; accumulation waits for all of it.  Nothing is in flight
-    // across the loop edge, so a batch costs one memory round trip once its
-    // indices are known, and the first batch two.
-    const int n_batches = (len + kWave - 1) / kWave;
+    const char *feat = static_cast<const char *>(p.feat);
     int row0, didx0;
-    load_indices(p, start, min(kWave, len), lane, row0, didx0);
-
-    for (int b = 0; b < n_batches; ++b) {
-        const int nb = min(kWave, len - b * kWave);
-        const bool more = b + 1 < n_batches;                  // wave-uniform
-        const int my_chunk = row0 * G;
+    load_indices(p, t0, min(kWave, n), s.lane, row0, didx0);
+    for (int base = 0; base < n; base += kWave) {
+        const int nb = min(kWave, n - base);
+        const bool more = base + kWave < n;                // wave-uniform
+        const int my_chunk = row0 * s.G;
         DRaw draw = DRaw(0);
         int row1 = 0, didx1 = 0;
-        for (int s0 = 0; s0 < nb; s0 += SUB * PPW) {
+        for (int s0 = 0; s0 < nb; s0 += SUB * s.PPW) {
+            // Every lane loads an in-bounds row (lanes past the batch repeat
+            // its last point, k < G); slots without a point are skipped by
+            // exec mask when accumulating.  Only wave-uniform guards branch.
+            int rows[SUB];
+#pragma unroll
+            for (int u = 0; u < SUB; ++u)
+                rows[u] = __shfl(my_chunk, (s0 + u * s.PPW + s.g) & (kWave - 1));
             u32x4 v[SUB];
-            // Chunks of CH sub-iterations are branch-free: every lane loads an
-            // in-bounds row (lanes past the batch repeat its last point, k < G),
-            // slots without a point are zeroed by select at first use, so the
-            // shuffles and loads of a chunk issue back to back.  Only the chunk
-            // guard, which is wave-uniform, branches.
 #pragma unroll
-            for (int c = 0; c < SUB; c += CH) {
-                if (s0 + c * PPW < nb) {
-#pragma unroll
-                    for (int u = c; u < c + CH && u < SUB; ++u) {
-                        const int j = s0 + u * PPW + g;
-                        const int row = __shfl(my_chunk, j & (kWave - 1));
-                        v[u] = feat[row + k];
-                    }
-                }
-            }
+            for (int u = 0; u < SUB; ++u)
+                if (s0 + u * s.PPW < nb)
+                    v[u] = *reinterpret_cast<const u32x4 *>(feat + uint32_t(rows[u] + s.k) * 16u);
             if (s0 == 0) {
                 draw = depth[didx0];
                 if (more)
-                    load_indices(p, start + (b + 1) * kWave, min(kWave, len - (b + 1) * kWave),
-                                 lane, row1, didx1);
+                    load_indices(p, t0 + base + kWave, min(kWave, n - base - kWave), s.lane, row1,
+                                 didx1);
             }
-            // depth values and the validity selects are first needed here
             const float my_d = static_cast<float>(draw);
+            float ds[SUB];
 #pragma unroll
-            for (int c = 0; c < SUB; c += CH) {
-                if (s0 + c * PPW < nb) {
+            for (int u = 0; u < SUB; ++u) ds[u] = __shfl(my_d, (s0 + u * s.PPW + s.g) & (kWave - 1));
 #pragma unroll
-                    for (int u = c; u < c + CH && u < SUB; ++u) {
-                        const int j = s0 + u * PPW + g;
-                        const float d = __shfl(my_d, j & (kWave - 1));
-                        const bool ok = slot_ok && j < nb;
-                        accumulate<FT>(acc, ok ? d : 0.f, ok ? v[u] : u32x4{0u, 0u, 0u, 0u});
-                    }
+            for (int u = 0; u < SUB; ++u) {
+                if (s0 + u * s.PPW < nb) {
+                    if (s.ok && s0 + u * s.PPW + s.g < nb) accumulate<FT>(acc, ds[u], v[u]);
                 }
             }
         }
         row0 = row1;
         didx0 = didx1;
     }
-    if (FT == kE4M3) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] *= p.feat_scale;
-    }
+}
 
-    // sum the PPW partial rows: red[w][g*C + k*E + e]
-    float *r = red[wv];
-    if (slot_ok) {
+// Folds the PPW slot accumulators of a wave through its LDS scratch r and
+// hands float4 q of the C-float row sum to emit(q, sum) on lane q (mod 64).
+template <int E, class Emit>
+__device__ inline void fold_slots(float *r, const float *acc, const Slots &s, int C, Emit emit)
+{
+    if (s.ok) {
 #pragma unroll
         for (int e = 0; e < E; e += 4)
-            *reinterpret_cast<f32x4 *>(r + g * C + k * E + e) = f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+            *reinterpret_cast<f32x4 *>(r + s.g * C + s.k * E + e) =
+                f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int q = s.lane; q < C / 4; q += kWave) {
+        f32x4 sum = *reinterpret_cast<const f32x4 *>(r + 4 * q);
+        for (int gg = 1; gg < s.PPW; ++gg) sum += *reinterpret_cast<const f32x4 *>(r + gg * C + 4 * q);
+        emit(q, sum);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
-    const int bev = p.ranks_bev[start];
-    const int prev_bev = iv > 0 ? p.ranks_bev[start - 1] : -1;
+// G_CT > 0: lanes per point fixed at compile time; G_CT == 0: p.chunks.
+template <int DT, int FT, int G_CT>
+__global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
+{
+    constexpr int E = Chunk<FT>::kElems;
+    constexpr int PPW_CT = G_CT > 0 ? kWave / G_CT : 1;
+    // rows in flight per lane: about 30 points per request round, capped so
+    // a wave stays near 64 VGPRs (eight waves per SIMD)
+    constexpr int SUB_RAW = G_CT > 0 ? (30 + PPW_CT - 1) / PPW_CT : 4;
+    constexpr int SUB = SUB_RAW > 8 ? 8 : (SUB_RAW > 5 && E == 16 ? 5 : SUB_RAW);
+    __shared__ __attribute__((aligned(16))) float red[kWavesPerBlock][kWave * E];
+    extern __shared__ __attribute__((aligned(16))) float part[];   // [kWavesPerBlock][C]
+
+    const int C = p.C, C4 = C / 4;
+    const int lane = __lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    Slots s;
+    s.G = G_CT > 0 ? G_CT : p.chunks;
+    s.PPW = G_CT > 0 ? PPW_CT : kWave / s.G;
+    s.g = lane / s.G;
+    s.k = lane - s.g * s.G;
+    s.lane = lane;
+    s.ok = s.g < s.PPW;
+    const float scale = FT == kE4M3 ? p.feat_scale : 1.f;
     f32x4 *o = reinterpret_cast<f32x4 *>(p.out);
-    const int C4 = C / 4;
-    for (int q = lane; q < C4; q += kWave) {
-        f32x4 s = *reinterpret_cast<const f32x4 *>(r + 4 * q);
-        for (int gg = 1; gg < PPW; ++gg) s += *reinterpret_cast<const f32x4 *>(r + gg * C + 4 * q);
-        __builtin_nontemporal_store(s, o + bev * C4 + q);
+    float acc[E];
+
+    if (int(blockIdx.x) >= p.n_long_blocks) {
+        // ---- short-interval role: one wave, one interval ----
+        const int iv = (blockIdx.x - p.n_long_blocks) * kWavesPerBlock + wv;
+        if (iv >= p.n_intervals) return;
+        const int start = p.interval_starts[iv];
+        const int len = p.interval_lengths[iv];
+        if (len > kShortMax) return;                       // owned by a long-interval block
+        // lane 0: the cell before this interval, other lanes: its own cell
+        const int cells = p.ranks_bev[max(start - 1 + min(lane, 1), 0)];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = 0.f;
+        accumulate_points<DT, FT, SUB>(p, start, len, s, acc);
+        const int bev = __builtin_amdgcn_readlane(cells, 1);
+        fold_slots<E>(red[wv], acc, s, C, [&](int q, f32x4 sum) {
+            if (FT == kE4M3) sum *= scale;
+            __builtin_nontemporal_store(sum, o + bev * C4 + q);
+        });
+        const int prev_bev = iv > 0 ? __builtin_amdgcn_readlane(cells, 0) : -1;
+        zero_cells(p.out, C, prev_bev + 1, bev, lane, kWave);
+        if (iv == p.n_intervals - 1) zero_cells(p.out, C, bev + 1, p.n_cells, lane, kWave);
+        return;
     }
 
-    zero_cells(p.out, C, prev_bev + 1, bev, lane);
-    if (iv == p.n_intervals - 1) zero_cells(p.out, C, bev + 1, p.n_cells, lane);
+    // ---- long-interval role: block b owns the long intervals b, b+n, ... ----
+    const int nl = p.n_long_blocks;
+    for (int base = blockIdx.x; base < p.n_intervals; base += nl * kWave) {
+        const int cand = base + lane * nl;
+        const int cand_len = cand < p.n_intervals ? p.interval_lengths[cand] : 0;
+        uint64_t todo = __ballot(cand_len > kShortMax);    // same in every wave of the block
+        while (todo) {
+            const int j = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            const int iv = base + j * nl;
+            const int len = __builtin_amdgcn_readlane(cand_len, j);
+            const int start = p.interval_starts[iv];
+            // the four waves take consecutive quarters of the points
+            const int quarter = (len + kWavesPerBlock - 1) / kWavesPerBlock;
+            const int lo = min(len, wv * quarter), hi = min(len, lo + quarter);
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] = 0.f;
+            if (lo < hi) accumulate_points<DT, FT, SUB>(p, start + lo, hi - lo, s, acc);
+            fold_slots<E>(red[wv], acc, s, C, [&](int q, f32x4 sum) {
+                *reinterpret_cast<f32x4 *>(part + wv * C + 4 * q) = sum;
+            });
+            __syncthreads();
+            const int bev = p.ranks_bev[start];
+            const int prev_bev = iv > 0 ? p.ranks_bev[start - 1] : -1;
+            for (int q = threadIdx.x; q < C4; q += kBlock) {
+                f32x4 sum = *reinterpret_cast<const f32x4 *>(part + 4 * q);
+#pragma unroll
+                for (int w = 1; w < kWavesPerBlock; ++w)
+                    sum += *reinterpret_cast<const f32x4 *>(part + w * C + 4 * q);
+                if (FT == kE4M3) sum *= scale;
+                __builtin_nontemporal_store(sum, o + bev * C4 + q);
+            }
+            zero_cells(p.out, C, prev_bev + 1, bev, threadIdx.x, kBlock);
+            if (iv == p.n_intervals - 1) zero_cells(p.out, C, bev + 1, p.n_cells, threadIdx.x, kBlock);
+            __syncthreads();                                // part is reused
+        }
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void zero_fill(f32x4 *out, int n4)
@@ -247,15 +302,18 @@ __global__ __launch_bounds__(kBlock) void zero_fill(f32x4 *out, int n4)
 }
 
 template <int DT, int FT>
-hipError_t launch_typed(const FwdParams &p, hipStream_t s)
+hipError_t launch_typed(FwdParams p, hipStream_t s)
 {
-    const int blocks = (p.n_intervals + kWavesPerBlock - 1) / kWavesPerBlock;
+    // long-interval blocks: about 32 intervals scanned per block, at most 2048
+    p.n_long_blocks = min(2048, max(1, (p.n_intervals + 31) / 32));
+    const int blocks = p.n_long_blocks + (p.n_intervals + kWavesPerBlock - 1) / kWavesPerBlock;
+    const size_t lds = size_t(kWavesPerBlock) * p.C * sizeof(float);
 #define BEVPOOL_CASE(GV)                                                    \
-    case GV: bev_pool_fwd<DT, FT, GV><<<blocks, kBlock, 0, s>>>(p); break;
+    case GV: bev_pool_fwd<DT, FT, GV><<<blocks, kBlock, lds, s>>>(p); break;
     switch (p.chunks) {
         BEVPOOL_CASE(1) BEVPOOL_CASE(2) BEVPOOL_CASE(4) BEVPOOL_CASE(5) BEVPOOL_CASE(8)
         BEVPOOL_CASE(10) BEVPOOL_CASE(16) BEVPOOL_CASE(20) BEVPOOL_CASE(32) BEVPOOL_CASE(64)
-    default: bev_pool_fwd<DT, FT, 0><<<blocks, kBlock, 0, s>>>(p); break;
+    default: bev_pool_fwd<DT, FT, 0><<<blocks, kBlock, lds, s>>>(p); break;
     }
 #undef BEVPOOL_CASE
     return hipGetLastError();
