@@ -10,9 +10,9 @@
 // arrays carry explicit indices so nothing is divided at run time.
 //
 // CDNA4 mapping (our design, not the pages'):
-//   * A feature row is split into G = rowbytes/16 chunks of 16 bytes; lane
-//     (g, k) = g*G + k loads chunk k of point slot g, so one wave
-//     instruction gathers PPW = 64/G rows with dwordx4 loads (C=80 fp16:
+//   * A feature row is split into G chunks of 16 bytes (8 bytes for e4m3 rows
+//     up to 512 bytes); lane (g, k) = g*G + k loads chunk k of point slot g,
+//     so one wave instruction gathers PPW = 64/G rows (C=80 fp16 or e4m3:
 //     G=10, six rows per instruction).  Row loads use a scalar base and a
 //     32-bit per-lane byte offset.
 //   * The map indices of up to 64 points come in with one coalesced load per
@@ -31,9 +31,10 @@
 //
 // The kernel is latency-bound (a 209K-point frame moves ~10 MB through HBM),
 // so the launch is shaped for memory-level parallelism:
-//   * Short intervals (<= 64 points, ~98% of them) get one wave each, in
-//     blocks of four, with a small register budget so eight waves fit per
-//     SIMD.
+//   * Short intervals (<= 96 points, ~99% of them at 209K points) get one
+//     wave each, in blocks of four, with a small register budget (about 18
+//     points' rows in flight per request round) so seven or eight waves fit
+//     per SIMD.
 //   * Long intervals (cells near the cameras, clustered in cell order) would
 //     each pin one wave for many round trips.  The first n_long_blocks blocks
 //     therefore own them instead: block b takes the long intervals b, b+n,
@@ -58,45 +59,56 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = kWave * kWavesPerBlock;
-constexpr int kShortMax = 64;   // longest interval a single wave owns
+constexpr int kShortMax = 96;   // longest interval a single wave owns
+constexpr int kRoundPoints = 18; // points per row-request round of a wave
+constexpr int kLongScan = 16;    // intervals scanned per long-interval block
 
-// Element types of one 16-byte chunk.
-template <int FT> struct Chunk;
-template <> struct Chunk<kF32> { static constexpr int kElems = 4; };
-template <> struct Chunk<kF16> { static constexpr int kElems = 8; };
-template <> struct Chunk<kE4M3> { static constexpr int kElems = 16; };
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// A lane's share of a feature row: CB bytes (16, or 8 for e4m3 rows up to
+// 512 bytes, which keeps e4m3 on the same ten-lane row geometry as fp16).
+template <int CB> struct ChunkVec;
+template <> struct ChunkVec<16> { using type = u32x4; };
+template <> struct ChunkVec<8> { using type = u32x2; };
+constexpr int elem_bytes(int ft) { return ft == kF32 ? 4 : ft == kF16 ? 2 : 1; }
 
 // Depth values are gathered in their storage type and widened at first use.
 template <int DT> struct DepthT;
 template <> struct DepthT<kF32> { using type = float; };
 template <> struct DepthT<kF16> { using type = _Float16; };
 
-// acc[e] += d * value(e) for the elements of one 16-byte chunk.
-template <int FT> __device__ inline void accumulate(float *acc, float d, u32x4 v);
-template <> __device__ inline void accumulate<kF32>(float *acc, float d, u32x4 v)
-{
-    const f32x4 f = __builtin_bit_cast(f32x4, v);   // whole-vector cast
+// acc[e] += d * value(e) for the elements of one chunk.
+template <int FT, int CB> struct Accum;
+template <> struct Accum<kF32, 16> {
+    __device__ static inline void run(float *acc, float d, u32x4 v)
+    {
+        const f32x4 f = __builtin_bit_cast(f32x4, v);   // whole-vector cast
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(d, f[e], acc[e]);
-}
-template <> __device__ inline void accumulate<kF16>(float *acc, float d, u32x4 v)
-{
-    const f16x8 h = __builtin_bit_cast(f16x8, v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(d, static_cast<float>(h[e]), acc[e]);
-}
-template <> __device__ inline void accumulate<kE4M3>(float *acc, float d, u32x4 v)
-{
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(v[w]), false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(v[w]), true);
-        acc[4 * w + 0] = __builtin_fmaf(d, lo[0], acc[4 * w + 0]);
-        acc[4 * w + 1] = __builtin_fmaf(d, lo[1], acc[4 * w + 1]);
-        acc[4 * w + 2] = __builtin_fmaf(d, hi[0], acc[4 * w + 2]);
-        acc[4 * w + 3] = __builtin_fmaf(d, hi[1], acc[4 * w + 3]);
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(d, f[e], acc[e]);
     }
-}
+};
+template <> struct Accum<kF16, 16> {
+    __device__ static inline void run(float *acc, float d, u32x4 v)
+    {
+        const f16x8 h = __builtin_bit_cast(f16x8, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(d, static_cast<float>(h[e]), acc[e]);
+    }
+};
+template <int CB> struct Accum<kE4M3, CB> {
+    template <class V> __device__ static inline void run(float *acc, float d, V v)
+    {
+#pragma unroll
+        for (int w = 0; w < CB / 4; ++w) {
+            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(v[w]), false);
+            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(v[w]), true);
+            acc[4 * w + 0] = __builtin_fmaf(d, lo[0], acc[4 * w + 0]);
+            acc[4 * w + 1] = __builtin_fmaf(d, lo[1], acc[4 * w + 1]);
+            acc[4 * w + 2] = __builtin_fmaf(d, hi[0], acc[4 * w + 2]);
+            acc[4 * w + 3] = __builtin_fmaf(d, hi[1], acc[4 * w + 3]);
+        }
+    }
+};
 
 // Zeroes cells [cell_lo, cell_hi) of out with non-temporal stores; `lane`
 // and `lanes` give this thread's position among the cooperating threads.
@@ -131,10 +143,11 @@ struct Slots {
 // only the row indices), then the batch's depth values, then the indices of
 // the next batch; accumulation waits for all of it.  Rows of a batch are
 // requested SUB sub-iterations (SUB*PPW points) at a time.
-template <int DT, int FT, int SUB>
+template <int DT, int FT, int CB, int SUB>
 __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, const Slots &s,
                                          float *acc)
 {
+    using V = typename ChunkVec<CB>::type;
     using DRaw = typename DepthT<DT>::type;
     const DRaw *depth = static_cast<const DRaw *>(p.depth);
     const char *feat = static_cast<const char *>(p.feat);
@@ -154,11 +167,11 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
 #pragma unroll
             for (int u = 0; u < SUB; ++u)
                 rows[u] = __shfl(my_chunk, (s0 + u * s.PPW + s.g) & (kWave - 1));
-            u32x4 v[SUB];
+            V v[SUB];
 #pragma unroll
             for (int u = 0; u < SUB; ++u)
                 if (s0 + u * s.PPW < nb)
-                    v[u] = *reinterpret_cast<const u32x4 *>(feat + uint32_t(rows[u] + s.k) * 16u);
+                    v[u] = *reinterpret_cast<const V *>(feat + uint32_t(rows[u] + s.k) * uint32_t(CB));
             if (s0 == 0) {
                 draw = depth[didx0];
                 if (more)
@@ -172,7 +185,7 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
 #pragma unroll
             for (int u = 0; u < SUB; ++u) {
                 if (s0 + u * s.PPW < nb) {
-                    if (s.ok && s0 + u * s.PPW + s.g < nb) accumulate<FT>(acc, ds[u], v[u]);
+                    if (s.ok && s0 + u * s.PPW + s.g < nb) Accum<FT, CB>::run(acc, ds[u], v[u]);
                 }
             }
         }
@@ -205,15 +218,16 @@ __device__ inline void fold_slots(float *r, const float *acc, const Slots &s, in
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// G_CT > 0: lanes per point fixed at compile time; G_CT == 0: p.chunks.
-template <int DT, int FT, int G_CT>
+// CB: bytes per lane chunk.  G_CT > 0: lanes per point (chunks per row)
+// fixed at compile time; G_CT == 0: p.chunks.
+template <int DT, int FT, int CB, int G_CT>
 __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
 {
-    constexpr int E = Chunk<FT>::kElems;
+    constexpr int E = CB / elem_bytes(FT);   // row elements per lane
     constexpr int PPW_CT = G_CT > 0 ? kWave / G_CT : 1;
-    // rows in flight per lane: about 30 points per request round, capped so
-    // a wave stays near 64 VGPRs (eight waves per SIMD)
-    constexpr int SUB_RAW = G_CT > 0 ? (30 + PPW_CT - 1) / PPW_CT : 4;
+    // rows in flight per lane: about kRoundPoints points per request round,
+    // which keeps the common kernels near 64 VGPRs (up to eight waves per SIMD)
+    constexpr int SUB_RAW = G_CT > 0 ? (kRoundPoints + PPW_CT - 1) / PPW_CT : 4;
     constexpr int SUB = SUB_RAW > 8 ? 8 : (SUB_RAW > 5 && E == 16 ? 5 : SUB_RAW);
     __shared__ __attribute__((aligned(16))) float red[kWavesPerBlock][kWave * E];
     extern __shared__ __attribute__((aligned(16))) float part[];   // [kWavesPerBlock][C]
@@ -243,7 +257,7 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
         const int cells = p.ranks_bev[max(start - 1 + min(lane, 1), 0)];
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[e] = 0.f;
-        accumulate_points<DT, FT, SUB>(p, start, len, s, acc);
+        accumulate_points<DT, FT, CB, SUB>(p, start, len, s, acc);
         const int bev = __builtin_amdgcn_readlane(cells, 1);
         fold_slots<E>(red[wv], acc, s, C, [&](int q, f32x4 sum) {
             if (FT == kE4M3) sum *= scale;
@@ -272,7 +286,7 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
             const int lo = min(len, wv * quarter), hi = min(len, lo + quarter);
 #pragma unroll
             for (int e = 0; e < E; ++e) acc[e] = 0.f;
-            if (lo < hi) accumulate_points<DT, FT, SUB>(p, start + lo, hi - lo, s, acc);
+            if (lo < hi) accumulate_points<DT, FT, CB, SUB>(p, start + lo, hi - lo, s, acc);
             fold_slots<E>(red[wv], acc, s, C, [&](int q, f32x4 sum) {
                 *reinterpret_cast<f32x4 *>(part + wv * C + 4 * q) = sum;
             });
@@ -301,19 +315,19 @@ __global__ __launch_bounds__(kBlock) void zero_fill(f32x4 *out, int n4)
         __builtin_nontemporal_store(z, out + i);
 }
 
-template <int DT, int FT>
+template <int DT, int FT, int CB>
 hipError_t launch_typed(FwdParams p, hipStream_t s)
 {
-    // long-interval blocks: about 32 intervals scanned per block, at most 2048
-    p.n_long_blocks = min(2048, max(1, (p.n_intervals + 31) / 32));
+    // long-interval blocks: about kLongScan intervals scanned per block
+    p.n_long_blocks = min(2048, max(1, (p.n_intervals + kLongScan - 1) / kLongScan));
     const int blocks = p.n_long_blocks + (p.n_intervals + kWavesPerBlock - 1) / kWavesPerBlock;
     const size_t lds = size_t(kWavesPerBlock) * p.C * sizeof(float);
-#define BEVPOOL_CASE(GV)                                                    \
-    case GV: bev_pool_fwd<DT, FT, GV><<<blocks, kBlock, lds, s>>>(p); break;
+#define BEVPOOL_CASE(GV)                                                        \
+    case GV: bev_pool_fwd<DT, FT, CB, GV><<<blocks, kBlock, lds, s>>>(p); break;
     switch (p.chunks) {
         BEVPOOL_CASE(1) BEVPOOL_CASE(2) BEVPOOL_CASE(4) BEVPOOL_CASE(5) BEVPOOL_CASE(8)
         BEVPOOL_CASE(10) BEVPOOL_CASE(16) BEVPOOL_CASE(20) BEVPOOL_CASE(32) BEVPOOL_CASE(64)
-    default: bev_pool_fwd<DT, FT, 0><<<blocks, kBlock, lds, s>>>(p); break;
+    default: bev_pool_fwd<DT, FT, CB, 0><<<blocks, kBlock, lds, s>>>(p); break;
     }
 #undef BEVPOOL_CASE
     return hipGetLastError();
@@ -329,9 +343,24 @@ hipError_t run_forward(const FwdParams &p, hipStream_t s)
         zero_fill<<<blocks, kBlock, 0, s>>>(reinterpret_cast<f32x4 *>(p.out), n4);
         return hipGetLastError();
     }
-    if (p.depth_dtype == kF32 && p.feat_dtype == kF32) return launch_typed<kF32, kF32>(p, s);
-    if (p.depth_dtype == kF16 && p.feat_dtype == kF16) return launch_typed<kF16, kF16>(p, s);
-    if (p.depth_dtype == kF16 && p.feat_dtype == kE4M3) return launch_typed<kF16, kE4M3>(p, s);
+    const int row_bytes = p.C * elem_bytes(p.feat_dtype);
+    FwdParams q = p;
+    if (p.depth_dtype == kF32 && p.feat_dtype == kF32) {
+        q.chunks = row_bytes / 16;
+        return launch_typed<kF32, kF32, 16>(q, s);
+    }
+    if (p.depth_dtype == kF16 && p.feat_dtype == kF16) {
+        q.chunks = row_bytes / 16;
+        return launch_typed<kF16, kF16, 16>(q, s);
+    }
+    if (p.depth_dtype == kF16 && p.feat_dtype == kE4M3) {
+        if (row_bytes <= 8 * kWave) {
+            q.chunks = row_bytes / 8;
+            return launch_typed<kF16, kE4M3, 8>(q, s);
+        }
+        q.chunks = row_bytes / 16;
+        return launch_typed<kF16, kE4M3, 16>(q, s);
+    }
     return hipErrorInvalidValue;
 }
 

@@ -131,10 +131,10 @@ int bevpool_build_map(const int32_t *point_cell, int32_t n_img, int32_t D, int32
  *   feat_scale: dequantisation scale applied to FP8_E4M3 features (ignored
  *       for the other types).
  *   Supported pairs: (F32 depth, F32 feat); (F16 depth, F16 feat);
- *       (F16 depth, FP8_E4M3 feat).  One feature row must be a multiple of
- *       16 bytes and at most 1024 bytes: C % 4 == 0 and C <= 256 for F32,
- *       C % 8 == 0 and C <= 512 for F16, C % 16 == 0 and C <= 1024 for
- *       FP8_E4M3.  Anything else returns BEVPOOL_ERR_UNSUPPORTED.
+ *       (F16 depth, FP8_E4M3 feat).  Channels: C % 4 == 0 and C <= 256 for
+ *       F32; C % 8 == 0 and C <= 512 for F16; for FP8_E4M3, C % 8 == 0 up to
+ *       C = 512 and C % 16 == 0 up to C = 1024.  Anything else returns
+ *       BEVPOOL_ERR_UNSUPPORTED.
  *   ranks_*, interval_*: a map as produced by bevpool_build_map for this
  *       geometry (n_points, n_intervals entries).  The kernel trusts the map:
  *       indices outside depth / feat / out are undefined behaviour.

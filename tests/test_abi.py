@@ -78,7 +78,9 @@ def _fwd(lib, **kw):
     (dict(fdt=7), -2),
     (dict(C=12), -2),                           # 24-byte rows are not 16-byte chunks
     (dict(C=1024), -2),                         # 2 KB rows
-    (dict(fdt=dws.FP8_E4M3, C=8), -2),          # 8-byte fp8 rows
+    (dict(fdt=dws.FP8_E4M3, C=4), -2),          # 4-byte fp8 rows
+    (dict(fdt=dws.FP8_E4M3, C=520), -2),        # fp8 rows over 512 bytes must be 16-byte multiples
+    (dict(fdt=dws.FP8_E4M3, C=2048), -2),
     (dict(n_cells=1 << 26, C=64), -3),          # n_cells * C >= 2^31
     (dict(rows=1 << 26, C=64), -3),
     (dict(out=FAKE + 4), -1),                   # misaligned output
