@@ -52,6 +52,11 @@ def parse():
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--details", default=None, help="write extra measurements as JSON here")
+    ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
+                    default=None,
+                    help="(CPU) turn rocprofv3 csv output of this benchmark into a summary under "
+                         "profiles/ and update profiles/traffic.json, then exit")
+    ap.add_argument("--commands", default="", help="with --summarize: the commands that made the inputs")
     return ap.parse_args()
 
 
@@ -83,6 +88,89 @@ def traffic_for(workload_name: str):
     return ent.get("hbm_bytes_per_launch")
 
 
+def _read_csv(directory, suffix):
+    import csv
+    import glob
+    paths = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not paths:
+        raise FileNotFoundError(f"no *{suffix} under {directory}")
+    with open(paths[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_means(directory, counter):
+    """Mean counter value per dispatch, by kernel name (rocprofv3 --pmc csv)."""
+    sums, counts = {}, {}
+    for r in _read_csv(directory, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        k = r["Kernel_Name"]
+        sums[k] = sums.get(k, 0.0) + float(r["Counter_Value"])
+        counts[k] = counts.get(k, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def summarize(args):
+    """Write profiles/<kernel>_<workload>.md and update profiles/traffic.json."""
+    trace_dir, fetch_dir, write_dir, bench_json = args.summarize
+    with open(bench_json) as f:
+        bench = json.loads(f.read().strip().splitlines()[-1])
+    workload = bench["config"]["workload"]
+    stats = _read_csv(trace_dir, "kernel_stats.csv")
+    fwd = [r for r in stats if "bev_pool_fwd" in r["Name"]]
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+
+    def pick(d, key):
+        return next((v for k, v in d.items() if key in k), None)
+
+    fwd_fetch, fwd_write = pick(fetch, "bev_pool_fwd"), pick(write, "bev_pool_fwd")
+    copy_fetch = pick(fetch, "bitwise_not")   # the calibration copy: reads and writes copy_kib
+    copy_write = pick(write, "bitwise_not")
+    copy_kib = bench.get("secondary", {}).get("copy_calib_mib", 0) * 1024
+    f_scale = copy_kib / copy_fetch if copy_fetch and copy_kib else None
+    w_scale = copy_kib / copy_write if copy_write and copy_kib else None
+    traffic = None
+    if fwd_fetch is not None and fwd_write is not None and f_scale and w_scale:
+        traffic = int(round((fwd_fetch * f_scale + fwd_write * w_scale) * 1024))
+    avg_ns = float(fwd[0]["AverageNs"]) if fwd else None
+    name = "bev_pool_fwd"
+    lines = [f"# {name} on {workload} (MI355X, gfx950)", "",
+             "Commands (from the repository root):", "", "```", args.commands.strip(), "```", "",
+             "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+             "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in stats[:8]:
+        lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                     f"{r['MinNs']} | {r['MaxNs']} |")
+    lines += ["", "## Benchmark line (same build)", "",
+              f"- per call (HIP events, graph replay): {bench['us_per_call']} us",
+              f"- rocprof average kernel duration: {avg_ns / 1e3:.3f} us" if avg_ns else "- rocprof: n/a",
+              f"- algorithmic bytes per call: {bench['bytes']['algorithmic']}",
+              f"- effective bandwidth: {bench['value']} GB/s ({bench['pct_hbm_peak']} % of 8 TB/s)", "",
+              "## HBM traffic (rocprofv3 --pmc, one counter per run, KiB per dispatch)", "",
+              f"- forward FETCH_SIZE {fwd_fetch}, WRITE_SIZE {fwd_write}",
+              f"- plain copy of {copy_kib} KiB: FETCH_SIZE {copy_fetch}, WRITE_SIZE {copy_write}",
+              f"- calibration factors: fetch {f_scale}, write {w_scale}",
+              f"- forward HBM bytes per call (calibrated): {traffic}",
+              f"- kernel source sha256[:16]: {bench['secondary']['kernel_sha256_16']}", ""]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    out_md = os.path.join(ROOT, "profiles", f"{name}_{workload}.md")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+    rec = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    rec[workload] = {"kernel_sha256_16": bench["secondary"]["kernel_sha256_16"],
+                     "hbm_bytes_per_launch": traffic, "fetch_kib": fwd_fetch, "write_kib": fwd_write,
+                     "copy_calibration": {"kib": copy_kib, "fetch_kib": copy_fetch,
+                                          "write_kib": copy_write},
+                     "rocprof_avg_ns": avg_ns}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(f"wrote {out_md} and {TRAFFIC_FILE}")
+
+
 def cpu_baseline(wl, ref_map, b_alg, seconds):
     import oracle
     s = wl.spec
@@ -103,6 +191,9 @@ def cpu_baseline(wl, ref_map, b_alg, seconds):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the pooled forward has no cross-GPU step in "
               f"this build (asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -203,10 +294,12 @@ def main():
     eager_us = ev0.elapsed_time(ev1) / 200 * 1e3
 
     if args.copy_calib_mib:
+        # a plain streaming copy of known size (read n bytes, write n bytes) for
+        # calibrating the FETCH_SIZE / WRITE_SIZE counters
         src = torch.empty(args.copy_calib_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         for _ in range(10):
-            dst.copy_(src)
+            torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
 
     traffic = traffic_for(s.name)
@@ -242,6 +335,7 @@ def main():
                       "eager_back_to_back_us": round(eager_us, 3),
                       "map_build_ms": round(map_ms, 3),
                       "timed_region_wall_s": round(wall_s, 3),
+                      "copy_calib_mib": args.copy_calib_mib,
                       "kernel_sha256_16": kernel_hash()},
     }
     if not args.no_cpu:
