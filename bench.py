@@ -293,6 +293,24 @@ def main():
     torch.cuda.synchronize()
     eager_us = ev0.elapsed_time(ev1) / 200 * 1e3
 
+    # single-call latency (warm) and cold-cache latency: before each cold call a
+    # 512 MiB buffer is overwritten, which evicts the 256 MB Infinity Cache and
+    # the L2s, so inputs, map and output come from HBM
+    def one_call_us(flush=None):
+        if flush is not None:
+            flush.fill_(0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
+    single = [one_call_us() for _ in range(100)]
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = [one_call_us(flush) for _ in range(30)]
+    del flush
+
     if args.copy_calib_mib:
         # a plain streaming copy of known size (read n bytes, write n bytes) for
         # calibrating the FETCH_SIZE / WRITE_SIZE counters
@@ -333,6 +351,9 @@ def main():
                       "p10_us": round(float(np.percentile(trials, 10)), 3) if trials else None,
                       "p90_us": round(float(np.percentile(trials, 90)), 3) if trials else None,
                       "eager_back_to_back_us": round(eager_us, 3),
+                      "single_call_us_median": round(float(np.median(single)), 3),
+                      "cold_call_us_median": round(float(np.median(cold)), 3),
+                      "cold_GBps": round(b_alg / (float(np.median(cold)) * 1e-6) / 1e9, 1),
                       "map_build_ms": round(map_ms, 3),
                       "timed_region_wall_s": round(wall_s, 3),
                       "copy_calib_mib": args.copy_calib_mib,

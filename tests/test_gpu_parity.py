@@ -109,7 +109,7 @@ def test_map_rejects_bad_cell_and_small_capacity():
 
 
 # --------------------------------------------------------------- forward
-@pytest.mark.parametrize("k", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("k", [0, 1, 2, 3, 4, 5, 6, 7, 8])
 def test_forward_on_workloads(k):
     wl, s, ref = _workload_case(k)
     m = gpu_map(wl.point_cell, s.n_img, s.D, s.H, s.W, s.n_cells)
@@ -258,3 +258,63 @@ def test_forward_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for o in outs:
             assert torch.equal(o, eager), f"replay {rep} differs from eager"
+
+
+def _cells_with_lengths(rng, lengths, n_cells_extra=7, gaps=True):
+    """point_cell for a 1 x 1 x 1 x P frustum whose kept points form one
+    interval per requested length, in shuffled frustum order."""
+    P = int(sum(lengths)) + 5
+    n_cells = len(lengths) * (3 if gaps else 1) + n_cells_extra
+    cells = rng.choice(n_cells, size=len(lengths), replace=False)
+    pc = np.full(P, -1, np.int32)
+    pos = rng.permutation(P)[:sum(lengths)]
+    pc[pos] = np.repeat(cells, lengths).astype(np.int32)
+    return pc, P, n_cells
+
+
+LENGTH_CASES = [
+    ("f16", 80, [1, 2, 63, 64, 65, 95, 96, 97, 127, 128, 129, 200, 411, 1000]),
+    ("e4m3", 80, [1, 64, 65, 96, 97, 300, 1440]),
+    ("f32", 8, [1, 30, 64, 65, 97, 500]),
+    ("f16", 128, [64, 96, 97, 256, 700]),
+    ("f16", 96, [5, 64, 97, 333]),            # runtime lane-count path (12 chunks)
+    ("e4m3", 1024, [3, 97, 260]),             # 16-byte e4m3 chunks
+]
+
+
+@pytest.mark.parametrize("feat_dtype,C,lengths", LENGTH_CASES,
+                         ids=[f"{a}-C{b}" for a, b, _ in LENGTH_CASES])
+def test_forward_interval_length_boundaries(feat_dtype, C, lengths):
+    """Intervals on both sides of the one-wave / long-interval split and of
+    the 64-point index batches, in both block roles."""
+    rng = np.random.default_rng(sum(lengths) + C)
+    pc, P, n_cells = _cells_with_lengths(rng, lengths)
+    n_img, D, H, Wd = 1, 1, 1, P
+    depth, feat, scale = _make_inputs(rng, n_img, D, H, Wd, C, feat_dtype)
+    say(f"[lengths {feat_dtype} C={C}] {lengths}")
+    ref = oracle.build_map(pc, n_img, D, H, Wd, n_cells)
+    assert sorted(ref["interval_lengths"].tolist()) == sorted(lengths)
+    m = gpu_map(pc, n_img, D, H, Wd, n_cells)
+    assert_maps_equal(map_to_numpy(m), ref, "map")
+    out_ref, out_abs = oracle_reference(depth, feat, feat_dtype, scale, C, ref, n_cells)
+    got = gpu_forward(depth, feat, scale, m, n_cells, C)
+    check_forward(got, out_ref, out_abs, feat_dtype, ref["ranks_bev"], f"lengths {lengths}")
+
+
+def test_forward_clustered_long_intervals():
+    """Hundreds of long intervals next to each other (more than one per
+    long-interval block), mixed with short ones, plus empty gaps."""
+    rng = np.random.default_rng(21)
+    lengths = list(rng.integers(97, 400, size=300)) + list(rng.integers(1, 60, size=3000))
+    pc, P, n_cells = _cells_with_lengths(rng, [int(x) for x in lengths])
+    n_img, D, H, Wd = 1, 1, 1, P
+    depth, feat, scale = _make_inputs(rng, n_img, D, H, Wd, 80, "f16")
+    say(f"[clustered long] P={P} intervals={len(lengths)}")
+    ref = oracle.build_map(pc, n_img, D, H, Wd, n_cells)
+    m = gpu_map(pc, n_img, D, H, Wd, n_cells)
+    assert_maps_equal(map_to_numpy(m), ref, "map")
+    out_ref, out_abs = oracle_reference(depth, feat, "f16", scale, 80, ref, n_cells)
+    got = gpu_forward(depth, feat, scale, m, n_cells, 80)
+    check_forward(got, out_ref, out_abs, "f16", ref["ranks_bev"], "clustered long")
+    again = gpu_forward(depth, feat, scale, m, n_cells, 80)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32)), "not deterministic"

@@ -89,6 +89,16 @@ SPECS = {
                     None, "f16", "f16"),
     4: WorkloadSpec("batched4_c128_fp16", 4, 6, 59, 32, 88, 128, 256, 0.4, 1.0, 59.0,
                     1_600_000, "f16", "f16"),
+    # wider feature rows on the BEVDet-like geometry (the article's Table 1
+    # also measures 128- and 256-channel configurations)
+    5: WorkloadSpec("bevdet_c128_fp16", 1, 6, 59, 16, 44, 128, 128, 0.8, 1.0, 59.0,
+                    209_000, "f16", "f16"),
+    6: WorkloadSpec("bevdet_c256_fp16", 1, 6, 59, 16, 44, 256, 128, 0.8, 1.0, 59.0,
+                    209_000, "f16", "f16"),
+    7: WorkloadSpec("bevdet_c128_fp8", 1, 6, 59, 16, 44, 128, 128, 0.8, 1.0, 59.0,
+                    209_000, "f16", "e4m3"),
+    8: WorkloadSpec("bevdet_c256_fp8", 1, 6, 59, 16, 44, 256, 128, 0.8, 1.0, 59.0,
+                    209_000, "f16", "e4m3"),
 }
 
 
