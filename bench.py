@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--graph-chunk", type=int, default=50, help="forward calls per captured graph")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
+    ap.add_argument("--kernel", choices=["owned", "v2", "v2do"], default="owned",
+                    help="owned: bevpool_forward; v2 / v2do: the tile-outer / depth-outer baselines")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-oracle sample length")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -228,8 +230,15 @@ def main():
     stream = torch.cuda.current_stream()
     fargs = dws.forward_args(depth, feat, m, s.n_cells, out, wl.feat_scale, stream)
 
+    order = {"v2": dws.ORDER_TILE_OUTER, "v2do": dws.ORDER_DEPTH_OUTER}.get(args.kernel)
+
+    def call(a):
+        if order is None:
+            return lib.bevpool_forward(*a)
+        return lib.bevpool_forward_baseline(order, *a)
+
     def launch():
-        rc = lib.bevpool_forward(*fargs)
+        rc = call(fargs)
         if rc != 0:
             raise dws.BevPoolError("bevpool_forward", rc)
 
@@ -248,7 +257,7 @@ def main():
         with torch.cuda.graph(graph, stream=cap_stream):
             gargs = dws.forward_args(depth, feat, m, s.n_cells, out, wl.feat_scale, cap_stream)
             for _ in range(chunk):
-                rc = lib.bevpool_forward(*gargs)
+                rc = call(gargs)
                 if rc != 0:
                     raise dws.BevPoolError("bevpool_forward", rc)
         for _ in range(2):
@@ -338,7 +347,8 @@ def main():
         "config": {"workload": s.name, "cameras": s.n_cam, "frames": s.frames, "D": s.D,
                    "H": s.H, "W": s.W, "C": s.C, "bev_grid": [s.frames, s.G, s.G],
                    "scatter_points": N, "intervals": I, "feat_dtype": s.feat_dtype,
-                   "depth_dtype": s.depth_dtype, "timing": "eager" if graph is None else
+                   "depth_dtype": s.depth_dtype, "kernel": args.kernel,
+                   "timing": "eager" if graph is None else
                    f"hip graph replay, {chunk} calls per graph"},
         "us_per_call": round(us, 3),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),

@@ -17,12 +17,14 @@ import torch
 
 __all__ = ["BevPoolError", "BevMap", "F32", "F16", "FP8_E4M3", "library_path",
            "bevpool_status_string", "bevpool_version", "bevpool_build_map_workspace_size",
-           "bevpool_build_map", "bevpool_forward", "forward_args"]
+           "bevpool_build_map", "bevpool_forward", "bevpool_forward_baseline", "forward_args",
+           "ORDER_TILE_OUTER", "ORDER_DEPTH_OUTER"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libbevpool.so")
 
 F32, F16, FP8_E4M3 = 0, 1, 2
+ORDER_TILE_OUTER, ORDER_DEPTH_OUTER = 0, 1
 OK, ERR_CAPACITY = 0, -5
 
 _TORCH_DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.uint8: FP8_E4M3,
@@ -65,6 +67,8 @@ def _load():
     lib.bevpool_forward.restype = ctypes.c_int
     lib.bevpool_forward.argtypes = [vp, i32, i64, vp, i32, i64, i32, ctypes.c_float,
                                     vp, vp, vp, vp, vp, i32, i32, vp, i64, vp]
+    lib.bevpool_forward_baseline.restype = ctypes.c_int
+    lib.bevpool_forward_baseline.argtypes = [i32] + lib.bevpool_forward.argtypes
     _lib = lib
     return lib
 
@@ -179,4 +183,20 @@ def bevpool_forward(depth: torch.Tensor, feat: torch.Tensor, m: BevMap, n_cells:
     rc = lib.bevpool_forward(*forward_args(depth, feat, m, n_cells, out, feat_scale, stream))
     if rc != OK:
         raise BevPoolError("bevpool_forward", rc)
+    return out
+
+
+def bevpool_forward_baseline(order: int, depth: torch.Tensor, feat: torch.Tensor, m: BevMap,
+                             n_cells: int, feat_scale: float = 1.0,
+                             out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The article's earlier loop orders (ORDER_TILE_OUTER = V2-style,
+    ORDER_DEPTH_OUTER = V2+DO-style) with bevpool_forward's arguments and
+    results; a comparison baseline, not a fast path."""
+    lib = _load()
+    if out is None:
+        out = torch.empty((n_cells, feat.shape[-1]), dtype=torch.float32, device=feat.device)
+    rc = lib.bevpool_forward_baseline(order, *forward_args(depth, feat, m, n_cells, out,
+                                                           feat_scale, stream))
+    if rc != OK:
+        raise BevPoolError("bevpool_forward_baseline", rc)
     return out

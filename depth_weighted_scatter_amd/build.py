@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libbevpool.so")
 
-SOURCES = ["bevpool_api.cpp", "map_kernels.hip", "forward_kernels.hip"]
+SOURCES = ["bevpool_api.cpp", "map_kernels.hip", "forward_kernels.hip", "baseline_kernels.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 instructions.

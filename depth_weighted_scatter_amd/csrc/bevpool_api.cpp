@@ -95,14 +95,17 @@ int bevpool_build_map(const int32_t *point_cell, int32_t n_img, int32_t D, int32
     return BEVPOOL_OK;
 }
 
-int bevpool_forward(const void *depth, int32_t depth_dtype, int64_t n_depth,
-                    const void *feat, int32_t feat_dtype, int64_t n_feat_rows, int32_t C,
-                    float feat_scale,
-                    const int32_t *ranks_depth, const int32_t *ranks_feat,
-                    const int32_t *ranks_bev,
-                    const int32_t *interval_starts, const int32_t *interval_lengths,
-                    int32_t n_points, int32_t n_intervals,
-                    float *out, int64_t n_cells, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// Host-side validation shared by the forward entry points; fills p.
+int validate_forward(const void *depth, int32_t depth_dtype, int64_t n_depth, const void *feat,
+                     int32_t feat_dtype, int64_t n_feat_rows, int32_t C, float feat_scale,
+                     const int32_t *ranks_depth, const int32_t *ranks_feat,
+                     const int32_t *ranks_bev, const int32_t *interval_starts,
+                     const int32_t *interval_lengths, int32_t n_points, int32_t n_intervals,
+                     float *out, int64_t n_cells, bool tiles16, bevpool::FwdParams &p)
 {
     if (!out || n_cells <= 0 || C <= 0 || n_points < 0 || n_intervals < 0 ||
         n_intervals > n_points)
@@ -120,7 +123,7 @@ int bevpool_forward(const void *depth, int32_t depth_dtype, int64_t n_depth,
     // a row is split into 16-byte lane chunks (8-byte ones for e4m3 rows of
     // up to 512 bytes), at most 64 per row
     const int64_t row_bytes = int64_t(C) * fe;
-    const bool e4m3_small = feat_dtype == BEVPOOL_FP8_E4M3 && row_bytes <= 512;
+    const bool e4m3_small = !tiles16 && feat_dtype == BEVPOOL_FP8_E4M3 && row_bytes <= 512;
     if (row_bytes % (e4m3_small ? 8 : 16) != 0 || row_bytes > 1024) return BEVPOOL_ERR_UNSUPPORTED;
 
     if (n_cells * C > kInt32Limit || n_feat_rows * C > kInt32Limit || n_depth > kInt32Limit)
@@ -129,7 +132,7 @@ int bevpool_forward(const void *depth, int32_t depth_dtype, int64_t n_depth,
         (depth && !aligned(depth, uintptr_t(elem_bytes(depth_dtype)))))
         return BEVPOOL_ERR_INVALID_ARG;
 
-    bevpool::FwdParams p{};
+    p = bevpool::FwdParams{};
     p.depth = depth;
     p.feat = feat;
     p.feat_scale = feat_scale;
@@ -145,7 +148,52 @@ int bevpool_forward(const void *depth, int32_t depth_dtype, int64_t n_depth,
     p.n_cells = int32_t(n_cells);
     p.depth_dtype = depth_dtype;
     p.feat_dtype = feat_dtype;
+    return BEVPOOL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bevpool_forward(const void *depth, int32_t depth_dtype, int64_t n_depth,
+                    const void *feat, int32_t feat_dtype, int64_t n_feat_rows, int32_t C,
+                    float feat_scale,
+                    const int32_t *ranks_depth, const int32_t *ranks_feat,
+                    const int32_t *ranks_bev,
+                    const int32_t *interval_starts, const int32_t *interval_lengths,
+                    int32_t n_points, int32_t n_intervals,
+                    float *out, int64_t n_cells, hipStream_t stream)
+{
+    bevpool::FwdParams p;
+    const int st = validate_forward(depth, depth_dtype, n_depth, feat, feat_dtype, n_feat_rows, C,
+                                    feat_scale, ranks_depth, ranks_feat, ranks_bev,
+                                    interval_starts, interval_lengths, n_points, n_intervals,
+                                    out, n_cells, false, p);
+    if (st != BEVPOOL_OK) return st;
     return bevpool::run_forward(p, stream) == hipSuccess ? BEVPOOL_OK : BEVPOOL_ERR_HIP;
+}
+
+int bevpool_forward_baseline(int32_t order, const void *depth, int32_t depth_dtype,
+                             int64_t n_depth, const void *feat, int32_t feat_dtype,
+                             int64_t n_feat_rows, int32_t C, float feat_scale,
+                             const int32_t *ranks_depth, const int32_t *ranks_feat,
+                             const int32_t *ranks_bev, const int32_t *interval_starts,
+                             const int32_t *interval_lengths, int32_t n_points,
+                             int32_t n_intervals, float *out, int64_t n_cells,
+                             hipStream_t stream)
+{
+    if (order != BEVPOOL_ORDER_TILE_OUTER && order != BEVPOOL_ORDER_DEPTH_OUTER)
+        return BEVPOOL_ERR_INVALID_ARG;
+    bevpool::FwdParams p;
+    const int st = validate_forward(depth, depth_dtype, n_depth, feat, feat_dtype, n_feat_rows, C,
+                                    feat_scale, ranks_depth, ranks_feat, ranks_bev,
+                                    interval_starts, interval_lengths, n_points, n_intervals,
+                                    out, n_cells, true, p);
+    if (st != BEVPOOL_OK) return st;
+    return bevpool::run_forward_baseline(p, order == BEVPOOL_ORDER_TILE_OUTER, stream) ==
+                   hipSuccess
+               ? BEVPOOL_OK
+               : BEVPOOL_ERR_HIP;
 }
 
 }  // extern "C"

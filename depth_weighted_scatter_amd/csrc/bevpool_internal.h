@@ -47,4 +47,7 @@ struct FwdParams {
 
 hipError_t run_forward(const FwdParams &p, hipStream_t stream);
 
+// The article's earlier loop orders (comparison baselines, baseline_kernels.hip).
+hipError_t run_forward_baseline(const FwdParams &p, bool tile_outer, hipStream_t stream);
+
 }  // namespace bevpool

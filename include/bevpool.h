@@ -152,6 +152,40 @@ int bevpool_forward(const void *depth, int32_t depth_dtype, int64_t n_depth,
                     int32_t n_points, int32_t n_intervals,
                     float *out, int64_t n_cells, hipStream_t stream);
 
+/* Loop orders of bevpool_forward_baseline. */
+typedef enum bevpool_order {
+    BEVPOOL_ORDER_TILE_OUTER = 0,   /* V2-style: channel tiles outside the scatter loop */
+    BEVPOOL_ORDER_DEPTH_OUTER = 1   /* V2+DO-style: each interval visited once, all channels */
+} bevpool_order;
+
+/*
+ * bevpool_forward_baseline -- the two earlier traversal orders the article
+ * compares against (sections "How BEVPoolV3 lowers latency" and "Remove
+ * redundant scatter traffic", Table 1), for measuring on the same hardware
+ * what the interval-owned kernel gains.  Not a fast path.
+ *
+ * One thread owns one (interval, 16-byte channel tile) pair and walks the
+ * interval's points, loading its indices and depth value per tile; the output
+ * is zero-filled by a first kernel and each occupied cell stored once by a
+ * second.  With BEVPOOL_ORDER_TILE_OUTER the tiles are the slowest-varying
+ * thread index (every tile re-reads all indices); with
+ * BEVPOOL_ORDER_DEPTH_OUTER the tiles of one interval are neighbouring
+ * threads (each index fetched once per interval).
+ *
+ * Arguments, layouts and results are those of bevpool_forward (same
+ * tolerance), except that a feature row must be a multiple of 16 bytes for
+ * every dtype.  Asynchronous, no allocation.  Errors: as bevpool_forward, and
+ * INVALID_ARG for an unknown order.
+ */
+int bevpool_forward_baseline(int32_t order, const void *depth, int32_t depth_dtype,
+                             int64_t n_depth, const void *feat, int32_t feat_dtype,
+                             int64_t n_feat_rows, int32_t C, float feat_scale,
+                             const int32_t *ranks_depth, const int32_t *ranks_feat,
+                             const int32_t *ranks_bev, const int32_t *interval_starts,
+                             const int32_t *interval_lengths, int32_t n_points,
+                             int32_t n_intervals, float *out, int64_t n_cells,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

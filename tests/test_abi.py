@@ -113,3 +113,13 @@ def _map(lib, **kw):
 ])
 def test_build_map_rejects(lib, kw, code):
     assert _map(lib, **kw) == code
+
+
+def test_baseline_rejects(lib):
+    a = dict(depth=FAKE, ddt=dws.F16, n_depth=100, feat=FAKE, fdt=dws.F16, rows=10, C=80,
+             scale=1.0, rd=FAKE, rf=FAKE, rb=FAKE, st=FAKE, ln=FAKE, n_points=5, n_iv=2,
+             out=FAKE, n_cells=16, stream=None)
+    assert lib.bevpool_forward_baseline(7, *a.values()) == -1          # unknown order
+    b = dict(a, fdt=dws.FP8_E4M3, C=40)                                  # 40-byte rows
+    assert lib.bevpool_forward_baseline(0, *b.values()) == -2
+    assert lib.bevpool_forward_baseline(1, *dict(a, out=None).values()) == -1

@@ -318,3 +318,20 @@ def test_forward_clustered_long_intervals():
     check_forward(got, out_ref, out_abs, "f16", ref["ranks_bev"], "clustered long")
     again = gpu_forward(depth, feat, scale, m, n_cells, 80)
     assert np.array_equal(got.view(np.uint32), again.view(np.uint32)), "not deterministic"
+
+
+@pytest.mark.parametrize("k", [0, 1, 2, 3])
+@pytest.mark.parametrize("order", [dws.ORDER_TILE_OUTER, dws.ORDER_DEPTH_OUTER],
+                         ids=["tile_outer", "depth_outer"])
+def test_baseline_orders_on_workloads(k, order):
+    """The V2-style and V2+DO-style baselines compute the same pooled output."""
+    wl, s, ref = _workload_case(k)
+    out_ref, out_abs = oracle_reference(wl.depth, wl.feat, s.feat_dtype, wl.feat_scale, s.C, ref,
+                                        s.n_cells)
+    say(f"  baseline order {order} workload {k}")
+    out = torch.full((s.n_cells, s.C), float("nan"), dtype=torch.float32, device="cuda")
+    dws.bevpool_forward_baseline(order, to_gpu(wl.depth), to_gpu(wl.feat), map_from_numpy(ref),
+                                 s.n_cells, feat_scale=wl.feat_scale, out=out)
+    torch.cuda.synchronize()
+    check_forward(out.cpu().numpy(), out_ref, out_abs, s.feat_dtype, ref["ranks_bev"],
+                  f"baseline {order} workload {k}")
