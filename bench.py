@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--graph-chunk", type=int, default=50, help="forward calls per captured graph")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
+    ap.add_argument("--bags", type=int, default=None,
+                    help="benchmark bevpool_segment_reduce on embedding-bag workload k instead")
     ap.add_argument("--kernel", choices=["owned", "v2", "v2do"], default="owned",
                     help="owned: bevpool_forward; v2 / v2do: the tile-outer / depth-outer baselines")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-oracle sample length")
@@ -191,10 +193,76 @@ def cpu_baseline(wl, ref_map, b_alg, seconds):
             "cpu": platform.processor() or platform.machine()}
 
 
+def bench_bags(args):
+    """Weighted embedding bags through bevpool_segment_reduce (the same owner
+    kernel); algorithmic bytes N*(C*e_table + e_weight + 4) + 4*(bags + 1) +
+    bags*C*4."""
+    import numpy as np
+    import torch
+
+    import depth_weighted_scatter_amd as dws
+    import workloads
+
+    dev = torch.device("cuda:0")
+    b = workloads.make_bags(args.bags, args.seed)
+    s = b.spec
+    N = int(b.indices.size)
+    w = torch.from_numpy(b.weights).to(dev) if b.weights is not None else None
+    table = torch.from_numpy(b.table).to(dev)
+    idx = torch.from_numpy(b.indices).to(dev)
+    off = torch.from_numpy(b.offsets).to(dev)
+    out = torch.empty((s.n_bags, s.C), dtype=torch.float32, device=dev)
+    e_w = 0 if w is None else w.element_size()
+    b_alg = N * (s.C * ELEM_BYTES[s.table_dtype] + e_w + 4) + 4 * (s.n_bags + 1) + s.n_bags * s.C * 4
+    lib = dws._load()
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        dws.bevpool_segment_reduce(w, table, idx, off, b.table_scale, out)
+    K = args.steps
+    chunk = max(1, min(args.graph_chunk, K))
+    while K % chunk:
+        chunk -= 1
+    cap = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        a = dws.segment_reduce_args(w, table, idx, off, out, b.table_scale, cap)
+        for _ in range(chunk):
+            if lib.bevpool_segment_reduce(*a) != 0:
+                raise RuntimeError("bevpool_segment_reduce failed")
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K // chunk):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    gbs = b_alg / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "bevpool_segment_reduce µs/call + effective GB/s (% HBM peak), weighted embedding bags",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": f"{s.table_dtype} table, f32 accumulate/out",
+        "data": "synthetic (geometric bag lengths, skewed rows, N(0,1) table)",
+        "config": {"workload": s.name, "bags": s.n_bags, "points": N, "table_rows": s.n_rows,
+                   "C": s.C, "weighted": w is not None},
+        "us_per_call": round(ms * 1e3, 3), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "bytes": {"algorithmic": b_alg}}), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize:
         summarize(args)
+        return
+    if args.bags is not None:
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        bench_bags(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the pooled forward has no cross-GPU step in "

@@ -18,6 +18,7 @@ import torch
 __all__ = ["BevPoolError", "BevMap", "F32", "F16", "FP8_E4M3", "library_path",
            "bevpool_status_string", "bevpool_version", "bevpool_build_map_workspace_size",
            "bevpool_build_map", "bevpool_forward", "bevpool_forward_baseline", "forward_args",
+           "bevpool_segment_reduce", "segment_reduce_args",
            "ORDER_TILE_OUTER", "ORDER_DEPTH_OUTER"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -69,6 +70,9 @@ def _load():
                                     vp, vp, vp, vp, vp, i32, i32, vp, i64, vp]
     lib.bevpool_forward_baseline.restype = ctypes.c_int
     lib.bevpool_forward_baseline.argtypes = [i32] + lib.bevpool_forward.argtypes
+    lib.bevpool_segment_reduce.restype = ctypes.c_int
+    lib.bevpool_segment_reduce.argtypes = [vp, i32, vp, i32, i64, i32, ctypes.c_float,
+                                           vp, vp, i32, i32, vp, vp]
     _lib = lib
     return lib
 
@@ -199,4 +203,48 @@ def bevpool_forward_baseline(order: int, depth: torch.Tensor, feat: torch.Tensor
                                                            feat_scale, stream))
     if rc != OK:
         raise BevPoolError("bevpool_forward_baseline", rc)
+    return out
+
+
+def segment_reduce_args(weights: Optional[torch.Tensor], table: torch.Tensor,
+                        indices: torch.Tensor, offsets: torch.Tensor, out: torch.Tensor,
+                        table_scale: float = 1.0, stream=None) -> tuple:
+    """Validated, marshalled argument tuple for the C bevpool_segment_reduce."""
+    _check_device_tensor("table", table)
+    _check_device_tensor("indices", indices, torch.int32)
+    _check_device_tensor("offsets", offsets, torch.int32)
+    _check_device_tensor("out", out, torch.float32)
+    if table.dtype not in _TORCH_DTYPE_CODE:
+        raise TypeError(f"table dtype {table.dtype} is not supported")
+    C = table.shape[-1]
+    n_seg = offsets.numel() - 1
+    if n_seg < 0 or out.numel() != n_seg * C:
+        raise ValueError("out must be [len(offsets) - 1, C]")
+    if weights is not None:
+        _check_device_tensor("weights", weights)
+        if weights.numel() != indices.numel():
+            raise ValueError("weights and indices differ in length")
+        wdt, wptr = _TORCH_DTYPE_CODE[weights.dtype], weights.data_ptr()
+    else:
+        wdt, wptr = (F32 if table.dtype == torch.float32 else F16), None
+    return (wptr, wdt, table.data_ptr(), _TORCH_DTYPE_CODE[table.dtype], table.numel() // C, C,
+            float(table_scale), indices.data_ptr(), offsets.data_ptr(), n_seg, indices.numel(),
+            out.data_ptr(), _stream_ptr(stream))
+
+
+def bevpool_segment_reduce(weights: Optional[torch.Tensor], table: torch.Tensor,
+                           indices: torch.Tensor, offsets: torch.Tensor,
+                           table_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """out[s] = sum_{t in [offsets[s], offsets[s+1])} weights[t] * table[indices[t]]
+    (weights None = 1); fp32 [len(offsets) - 1, C].  Enqueued on the current
+    stream; never synchronises."""
+    lib = _load()
+    if out is None:
+        out = torch.empty((offsets.numel() - 1, table.shape[-1]), dtype=torch.float32,
+                          device=table.device)
+    rc = lib.bevpool_segment_reduce(*segment_reduce_args(weights, table, indices, offsets, out,
+                                                         table_scale, stream))
+    if rc != OK:
+        raise BevPoolError("bevpool_segment_reduce", rc)
     return out

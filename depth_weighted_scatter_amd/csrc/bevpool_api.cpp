@@ -196,4 +196,42 @@ int bevpool_forward_baseline(int32_t order, const void *depth, int32_t depth_dty
                : BEVPOOL_ERR_HIP;
 }
 
+int bevpool_segment_reduce(const void *weights, int32_t weight_dtype, const void *table,
+                           int32_t table_dtype, int64_t n_rows, int32_t C, float table_scale,
+                           const int32_t *indices, const int32_t *offsets, int32_t n_segments,
+                           int32_t n_points, float *out, hipStream_t stream)
+{
+    if (n_segments < 0 || n_points < 0 || C <= 0) return BEVPOOL_ERR_INVALID_ARG;
+    if (n_segments == 0) return BEVPOOL_OK;
+    if (!table || !indices || !offsets || !out || n_rows <= 0) return BEVPOOL_ERR_INVALID_ARG;
+    const int fe = elem_bytes(table_dtype);
+    const bool pair_ok = (weight_dtype == BEVPOOL_F32 && table_dtype == BEVPOOL_F32) ||
+                         (weight_dtype == BEVPOOL_F16 && table_dtype == BEVPOOL_F16) ||
+                         (weight_dtype == BEVPOOL_F16 && table_dtype == BEVPOOL_FP8_E4M3);
+    if (!pair_ok || fe == 0) return BEVPOOL_ERR_UNSUPPORTED;
+    const int64_t row_bytes = int64_t(C) * fe;
+    const bool e4m3_small = table_dtype == BEVPOOL_FP8_E4M3 && row_bytes <= 512;
+    if (row_bytes % (e4m3_small ? 8 : 16) != 0 || row_bytes > 1024) return BEVPOOL_ERR_UNSUPPORTED;
+    if (int64_t(n_segments) * C > kInt32Limit || n_rows * C > kInt32Limit)
+        return BEVPOOL_ERR_OVERFLOW;
+    if (!aligned(out, 16) || !aligned(table, 16) ||
+        (weights && !aligned(weights, uintptr_t(elem_bytes(weight_dtype)))))
+        return BEVPOOL_ERR_INVALID_ARG;
+
+    bevpool::FwdParams p{};
+    p.depth = weights;
+    p.feat = table;
+    p.feat_scale = table_scale;
+    p.C = C;
+    p.chunks = int32_t(row_bytes / 16);
+    p.ranks_feat = indices;
+    p.interval_starts = offsets;
+    p.n_intervals = n_segments;
+    p.out = out;
+    p.n_cells = n_segments;
+    p.depth_dtype = weight_dtype;
+    p.feat_dtype = table_dtype;
+    return bevpool::run_segment_reduce(p, stream) == hipSuccess ? BEVPOOL_OK : BEVPOOL_ERR_HIP;
+}
+
 }  // extern "C"

@@ -47,6 +47,11 @@ struct FwdParams {
 
 hipError_t run_forward(const FwdParams &p, hipStream_t stream);
 
+// Segment mode of the same kernel: interval_starts holds n_intervals + 1
+// offsets, cell i is segment i, depth (nullable) holds one weight per point,
+// and ranks_depth / ranks_bev / interval_lengths are unused.
+hipError_t run_segment_reduce(const FwdParams &p, hipStream_t stream);
+
 // The article's earlier loop orders (comparison baselines, baseline_kernels.hip).
 hipError_t run_forward_baseline(const FwdParams &p, bool tile_outer, hipStream_t stream);
 

@@ -124,12 +124,14 @@ __device__ inline void zero_cells(float *out, int C, int cell_lo, int cell_hi, i
 // Lane i reads the map indices of point t0 + min(i, n - 1), 1 <= n <= 64:
 // lanes past the batch repeat its last point, so every address derived from
 // them stays in bounds and no lane needs an exec-masked branch.
+// In segment mode (SEG) the weight of point t is read directly at t.
+template <bool SEG>
 __device__ inline void load_indices(const FwdParams &p, int t0, int n, int lane, int &row,
                                     int &didx)
 {
     const int t = t0 + min(lane, n - 1);
     row = __builtin_nontemporal_load(p.ranks_feat + t);
-    didx = __builtin_nontemporal_load(p.ranks_depth + t);
+    didx = SEG ? t : __builtin_nontemporal_load(p.ranks_depth + t);
 }
 
 // Lane geometry of a wave: lane (g, k) = g*G + k holds chunk k of slot g.
@@ -143,7 +145,7 @@ struct Slots {
 // only the row indices), then the batch's depth values, then the indices of
 // the next batch; accumulation waits for all of it.  Rows of a batch are
 // requested SUB sub-iterations (SUB*PPW points) at a time.
-template <int DT, int FT, int CB, int SUB>
+template <int DT, int FT, int CB, int SUB, bool SEG>
 __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, const Slots &s,
                                          float *acc)
 {
@@ -152,7 +154,7 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
     const DRaw *depth = static_cast<const DRaw *>(p.depth);
     const char *feat = static_cast<const char *>(p.feat);
     int row0, didx0;
-    load_indices(p, t0, min(kWave, n), s.lane, row0, didx0);
+    load_indices<SEG>(p, t0, min(kWave, n), s.lane, row0, didx0);
     for (int base = 0; base < n; base += kWave) {
         const int nb = min(kWave, n - base);
         const bool more = base + kWave < n;                // wave-uniform
@@ -173,10 +175,10 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
                 if (s0 + u * s.PPW < nb)
                     v[u] = *reinterpret_cast<const V *>(feat + uint32_t(rows[u] + s.k) * uint32_t(CB));
             if (s0 == 0) {
-                draw = depth[didx0];
+                draw = (SEG && !depth) ? DRaw(1) : depth[didx0];   // segments may be unweighted
                 if (more)
-                    load_indices(p, t0 + base + kWave, min(kWave, n - base - kWave), s.lane, row1,
-                                 didx1);
+                    load_indices<SEG>(p, t0 + base + kWave, min(kWave, n - base - kWave), s.lane,
+                                      row1, didx1);
             }
             const float my_d = static_cast<float>(draw);
             float ds[SUB];
@@ -220,7 +222,11 @@ __device__ inline void fold_slots(float *r, const float *acc, const Slots &s, in
 
 // CB: bytes per lane chunk.  G_CT > 0: lanes per point (chunks per row)
 // fixed at compile time; G_CT == 0: p.chunks.
-template <int DT, int FT, int CB, int G_CT>
+//
+// SEG: segment mode (bevpool_segment_reduce): interval i is segment i, with
+// start offsets[i] (interval_starts) and length offsets[i+1] - offsets[i]
+// (possibly 0), cell i, and the weight of point t read at t (or 1).
+template <int DT, int FT, int CB, int G_CT, bool SEG>
 __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
 {
     constexpr int E = CB / elem_bytes(FT);   // row elements per lane
@@ -251,13 +257,13 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
         const int iv = (blockIdx.x - p.n_long_blocks) * kWavesPerBlock + wv;
         if (iv >= p.n_intervals) return;
         const int start = p.interval_starts[iv];
-        const int len = p.interval_lengths[iv];
+        const int len = SEG ? p.interval_starts[iv + 1] - start : p.interval_lengths[iv];
         if (len > kShortMax) return;                       // owned by a long-interval block
         // lane 0: the cell before this interval, other lanes: its own cell
-        const int cells = p.ranks_bev[max(start - 1 + min(lane, 1), 0)];
+        const int cells = SEG ? iv - 1 + min(lane, 1) : p.ranks_bev[max(start - 1 + min(lane, 1), 0)];
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[e] = 0.f;
-        accumulate_points<DT, FT, CB, SUB>(p, start, len, s, acc);
+        if (!SEG || len > 0) accumulate_points<DT, FT, CB, SUB, SEG>(p, start, len, s, acc);
         const int bev = __builtin_amdgcn_readlane(cells, 1);
         fold_slots<E>(red[wv], acc, s, C, [&](int q, f32x4 sum) {
             if (FT == kE4M3) sum *= scale;
@@ -273,7 +279,10 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
     const int nl = p.n_long_blocks;
     for (int base = blockIdx.x; base < p.n_intervals; base += nl * kWave) {
         const int cand = base + lane * nl;
-        const int cand_len = cand < p.n_intervals ? p.interval_lengths[cand] : 0;
+        int cand_len = 0;
+        if (cand < p.n_intervals)
+            cand_len = SEG ? p.interval_starts[cand + 1] - p.interval_starts[cand]
+                           : p.interval_lengths[cand];
         uint64_t todo = __ballot(cand_len > kShortMax);    // same in every wave of the block
         while (todo) {
             const int j = __builtin_ctzll(todo);
@@ -286,13 +295,13 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
             const int lo = min(len, wv * quarter), hi = min(len, lo + quarter);
 #pragma unroll
             for (int e = 0; e < E; ++e) acc[e] = 0.f;
-            if (lo < hi) accumulate_points<DT, FT, CB, SUB>(p, start + lo, hi - lo, s, acc);
+            if (lo < hi) accumulate_points<DT, FT, CB, SUB, SEG>(p, start + lo, hi - lo, s, acc);
             fold_slots<E>(red[wv], acc, s, C, [&](int q, f32x4 sum) {
                 *reinterpret_cast<f32x4 *>(part + wv * C + 4 * q) = sum;
             });
             __syncthreads();
-            const int bev = p.ranks_bev[start];
-            const int prev_bev = iv > 0 ? p.ranks_bev[start - 1] : -1;
+            const int bev = SEG ? iv : p.ranks_bev[start];
+            const int prev_bev = SEG ? iv - 1 : (iv > 0 ? p.ranks_bev[start - 1] : -1);
             for (int q = threadIdx.x; q < C4; q += kBlock) {
                 f32x4 sum = *reinterpret_cast<const f32x4 *>(part + 4 * q);
 #pragma unroll
@@ -315,22 +324,46 @@ __global__ __launch_bounds__(kBlock) void zero_fill(f32x4 *out, int n4)
         __builtin_nontemporal_store(z, out + i);
 }
 
-template <int DT, int FT, int CB>
+template <int DT, int FT, int CB, bool SEG>
 hipError_t launch_typed(FwdParams p, hipStream_t s)
 {
     // long-interval blocks: about kLongScan intervals scanned per block
     p.n_long_blocks = min(2048, max(1, (p.n_intervals + kLongScan - 1) / kLongScan));
     const int blocks = p.n_long_blocks + (p.n_intervals + kWavesPerBlock - 1) / kWavesPerBlock;
     const size_t lds = size_t(kWavesPerBlock) * p.C * sizeof(float);
-#define BEVPOOL_CASE(GV)                                                        \
-    case GV: bev_pool_fwd<DT, FT, CB, GV><<<blocks, kBlock, lds, s>>>(p); break;
+#define BEVPOOL_CASE(GV)                                                             \
+    case GV: bev_pool_fwd<DT, FT, CB, GV, SEG><<<blocks, kBlock, lds, s>>>(p); break;
     switch (p.chunks) {
         BEVPOOL_CASE(1) BEVPOOL_CASE(2) BEVPOOL_CASE(4) BEVPOOL_CASE(5) BEVPOOL_CASE(8)
         BEVPOOL_CASE(10) BEVPOOL_CASE(16) BEVPOOL_CASE(20) BEVPOOL_CASE(32) BEVPOOL_CASE(64)
-    default: bev_pool_fwd<DT, FT, CB, 0><<<blocks, kBlock, lds, s>>>(p); break;
+    default: bev_pool_fwd<DT, FT, CB, 0, SEG><<<blocks, kBlock, lds, s>>>(p); break;
     }
 #undef BEVPOOL_CASE
     return hipGetLastError();
+}
+
+template <bool SEG>
+hipError_t dispatch(const FwdParams &p, hipStream_t s)
+{
+    const int row_bytes = p.C * elem_bytes(p.feat_dtype);
+    FwdParams q = p;
+    if (p.depth_dtype == kF32 && p.feat_dtype == kF32) {
+        q.chunks = row_bytes / 16;
+        return launch_typed<kF32, kF32, 16, SEG>(q, s);
+    }
+    if (p.depth_dtype == kF16 && p.feat_dtype == kF16) {
+        q.chunks = row_bytes / 16;
+        return launch_typed<kF16, kF16, 16, SEG>(q, s);
+    }
+    if (p.depth_dtype == kF16 && p.feat_dtype == kE4M3) {
+        if (row_bytes <= 8 * kWave) {
+            q.chunks = row_bytes / 8;
+            return launch_typed<kF16, kE4M3, 8, SEG>(q, s);
+        }
+        q.chunks = row_bytes / 16;
+        return launch_typed<kF16, kE4M3, 16, SEG>(q, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -343,25 +376,12 @@ hipError_t run_forward(const FwdParams &p, hipStream_t s)
         zero_fill<<<blocks, kBlock, 0, s>>>(reinterpret_cast<f32x4 *>(p.out), n4);
         return hipGetLastError();
     }
-    const int row_bytes = p.C * elem_bytes(p.feat_dtype);
-    FwdParams q = p;
-    if (p.depth_dtype == kF32 && p.feat_dtype == kF32) {
-        q.chunks = row_bytes / 16;
-        return launch_typed<kF32, kF32, 16>(q, s);
-    }
-    if (p.depth_dtype == kF16 && p.feat_dtype == kF16) {
-        q.chunks = row_bytes / 16;
-        return launch_typed<kF16, kF16, 16>(q, s);
-    }
-    if (p.depth_dtype == kF16 && p.feat_dtype == kE4M3) {
-        if (row_bytes <= 8 * kWave) {
-            q.chunks = row_bytes / 8;
-            return launch_typed<kF16, kE4M3, 8>(q, s);
-        }
-        q.chunks = row_bytes / 16;
-        return launch_typed<kF16, kE4M3, 16>(q, s);
-    }
-    return hipErrorInvalidValue;
+    return dispatch<false>(p, s);
+}
+
+hipError_t run_segment_reduce(const FwdParams &p, hipStream_t s)
+{
+    return dispatch<true>(p, s);
 }
 
 }  // namespace bevpool

@@ -152,6 +152,35 @@ int bevpool_forward(const void *depth, int32_t depth_dtype, int64_t n_depth,
                     int32_t n_points, int32_t n_intervals,
                     float *out, int64_t n_cells, hipStream_t stream);
 
+/*
+ * bevpool_segment_reduce -- the interval-owned kernel applied to a generic
+ * weighted segmented gather-reduce (an embedding bag with per-point weights).
+ * The article names sparse embeddings and segmented reductions as the same
+ * workload shape as BEV pooling (sections "Map the algorithm to hardware" and
+ * "Getting started"):
+ *
+ *   out[s, c] = sum over t in [offsets[s], offsets[s+1]) of
+ *               weights[t] * table[indices[t], c] (* table_scale for e4m3)
+ *
+ * with one owner per segment, fp32 accumulation and one write per output
+ * element; empty segments are written as 0.
+ *
+ *   weights [n_points] (device; NULL = all ones), weight_dtype as the depth
+ *       dtype of bevpool_forward.
+ *   table [n_rows, C] (device, 16-byte aligned), table_dtype and the
+ *       supported (weight, table, C) combinations as bevpool_forward.
+ *   indices [n_points] int32 rows of table; offsets [n_segments + 1] int32,
+ *       non-decreasing, offsets[n_segments] <= n_points.  The kernel trusts
+ *       them (values outside the arrays are undefined behaviour).
+ *   out [n_segments, C] fp32 (device, 16-byte aligned), overwritten.
+ * Asynchronous, no allocation.  n_segments == 0 is a no-op.  Errors:
+ * INVALID_ARG, UNSUPPORTED, OVERFLOW, HIP.
+ */
+int bevpool_segment_reduce(const void *weights, int32_t weight_dtype, const void *table,
+                           int32_t table_dtype, int64_t n_rows, int32_t C, float table_scale,
+                           const int32_t *indices, const int32_t *offsets, int32_t n_segments,
+                           int32_t n_points, float *out, hipStream_t stream);
+
 /* Loop orders of bevpool_forward_baseline. */
 typedef enum bevpool_order {
     BEVPOOL_ORDER_TILE_OUTER = 0,   /* V2-style: channel tiles outside the scatter loop */

@@ -51,6 +51,9 @@ def _bind(path: str):
     lib.oracle_forward.restype = ctypes.c_int
     lib.oracle_forward.argtypes = [vp, ctypes.c_int, i64, vp, ctypes.c_int, i64, i64,
                                    ctypes.c_double, vp, vp, vp, i64, i64, dp, dp]
+    lib.oracle_segment_reduce.restype = ctypes.c_int
+    lib.oracle_segment_reduce.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64,
+                                          ctypes.c_double, vp, vp, i64, dp, dp]
     return lib
 
 
@@ -138,4 +141,37 @@ def forward(depth: np.ndarray, feat: np.ndarray, feat_dtype: str, feat_scale: fl
                             _ptr(out), _ptr(out_abs) if with_abs else None)
     if rc != 0:
         raise ValueError(f"oracle_forward failed ({rc})")
+    return (out, out_abs) if with_abs else out
+
+
+def segment_reduce(weights, table: np.ndarray, table_dtype: str, table_scale: float,
+                   indices: np.ndarray, offsets: np.ndarray, with_abs: bool = False):
+    """out[s] = sum_{t in [offsets[s], offsets[s+1])} w[t] * table[indices[t]] in double.
+
+    weights: float32/float16 array [N] or None (all ones); table: [rows, C]
+    float32/float16 or uint8 e4m3 codes.
+    """
+    lib = _load()
+    table = np.ascontiguousarray(table)
+    C = table.shape[-1]
+    rows = table.size // C
+    tdt = _DTYPE_CODE[table_dtype]
+    expect = {F32: np.float32, F16: np.float16, E4M3: np.uint8}[tdt]
+    if table.dtype != expect:
+        raise TypeError(f"table dtype {table.dtype} does not match {table_dtype}")
+    idx = np.ascontiguousarray(indices, np.int32)
+    off = np.ascontiguousarray(offsets, np.int32)
+    n_seg = off.size - 1
+    wdt, wptr = 0, None
+    if weights is not None:
+        weights = np.ascontiguousarray(weights)
+        wdt = {np.dtype(np.float32): F32, np.dtype(np.float16): F16}[weights.dtype]
+        wptr = _ptr(weights)
+    out = np.empty((n_seg, C), np.float64)
+    out_abs = np.empty((n_seg, C), np.float64) if with_abs else None
+    rc = lib.oracle_segment_reduce(wptr, wdt, _ptr(table), tdt, rows, C, float(table_scale),
+                                   _ptr(idx), _ptr(off), n_seg, _ptr(out),
+                                   _ptr(out_abs) if with_abs else None)
+    if rc != 0:
+        raise ValueError(f"oracle_segment_reduce failed ({rc})")
     return (out, out_abs) if with_abs else out

@@ -31,7 +31,8 @@
  * Pins (tests/test_oracle_pins.py): all 65536 fp16 and 256 e4m3 codes
  * against numpy / torch and the format's closed form; the map against
  * numpy.lexsort and a hand-worked example; the forward against a dense
- * one-hot matrix product, closed forms and invariants.
+ * one-hot matrix product, closed forms and invariants; the segmented reduce
+ * against torch.nn.functional.embedding_bag and against the forward itself.
  */
 #include <math.h>
 #include <stdint.h>
@@ -174,6 +175,45 @@ int oracle_forward(const void *depth, int depth_dtype, int64_t n_depth,
             double term = d * (load_value(feat, feat_dtype, rf * C + c) * fscale);
             out[rb * C + c] += term;
             if (out_abs) out_abs[rb * C + c] += fabs(term);
+        }
+    }
+    return 0;
+}
+
+/*
+ * Weighted segmented gather-reduce, the same owner pattern applied to a
+ * generic table ("Accelerating BEV Pooling on NVIDIA GPUs for Physical AI
+ * Applications", section "Map the algorithm to hardware" and "Getting
+ * started", name sparse embeddings and segmented reductions as the same
+ * workload shape):
+ *   out[s, c] = sum over t in [offsets[s], offsets[s+1]) (increasing) of
+ *               w[t] * table[indices[t], c]
+ * with w[t] = 1 when weights is NULL and e4m3 table values read as
+ * e4m3(q) * table_scale.  Empty segments are 0.  out (and out_abs, the sum
+ * of |term|, optional) are [n_segments, C].  Returns 0, or -1 on a bad dtype,
+ * decreasing offsets or an index outside the table.
+ */
+int oracle_segment_reduce(const void *weights, int w_dtype, const void *table, int t_dtype,
+                          int64_t n_rows, int64_t C, double table_scale,
+                          const int32_t *indices, const int32_t *offsets, int64_t n_segments,
+                          double *out, double *out_abs)
+{
+    if (weights && (w_dtype < ORACLE_F32 || w_dtype > ORACLE_F16)) return -1;
+    if (t_dtype < ORACLE_F32 || t_dtype > ORACLE_E4M3) return -1;
+    double tscale = t_dtype == ORACLE_E4M3 ? table_scale : 1.0;
+    memset(out, 0, (size_t)(n_segments * C) * sizeof(double));
+    if (out_abs) memset(out_abs, 0, (size_t)(n_segments * C) * sizeof(double));
+    for (int64_t s = 0; s < n_segments; ++s) {
+        if (offsets[s + 1] < offsets[s]) return -1;
+        for (int64_t t = offsets[s]; t < offsets[s + 1]; ++t) {
+            int64_t r = indices[t];
+            if (r < 0 || r >= n_rows) return -1;
+            double w = weights ? load_value(weights, w_dtype, t) : 1.0;
+            for (int64_t c = 0; c < C; ++c) {
+                double term = w * (load_value(table, t_dtype, r * C + c) * tscale);
+                out[s * C + c] += term;
+                if (out_abs) out_abs[s * C + c] += fabs(term);
+            }
         }
     }
     return 0;

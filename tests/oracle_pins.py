@@ -275,9 +275,55 @@ def check_bad_cell_rejected():
         raise AssertionError("cell -2 was accepted")
 
 
+# ------------------------------------------------- segmented gather-reduce
+def check_segment_reduce_vs_embedding_bag(n_cases=12, seed=5):
+    """Against torch.nn.functional.embedding_bag (mode sum, per-sample
+    weights) in float64 -- a library routine with the same definition."""
+    rng = np.random.default_rng(seed)
+    for case in range(n_cases):
+        rows, C, n_seg = int(rng.integers(1, 40)), int(rng.choice([1, 4, 16])), int(rng.integers(1, 30))
+        lens = rng.integers(0, 12, size=n_seg)
+        off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        N = int(off[-1])
+        idx = rng.integers(0, rows, size=N).astype(np.int32)
+        fdt = ("f32", "f16", "e4m3")[case % 3]
+        table = rng.standard_normal((rows, C))
+        scale = 1.0
+        if fdt == "f32":
+            table = table.astype(np.float32)
+        elif fdt == "f16":
+            table = table.astype(np.float16)
+        else:
+            table, scale = W.quantize_e4m3(table)
+        w = rng.random(N).astype(np.float16) if case % 2 else None
+        got = oracle.segment_reduce(w, table, fdt, scale, idx, off)
+        tv = torch.from_numpy(_values(table, fdt, scale).reshape(rows, C))
+        psw = torch.from_numpy(w.astype(np.float64)) if w is not None else None
+        ref = torch.nn.functional.embedding_bag(torch.from_numpy(idx.astype(np.int64)), tv,
+                                                torch.from_numpy(off[:-1].astype(np.int64)),
+                                                mode="sum", per_sample_weights=psw).numpy()
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), f"case {case} differs from embedding_bag"
+
+
+def check_segment_reduce_is_bev_forward():
+    """The BEV forward is the segmented reduce with indices = ranks_feat,
+    weights = depth[ranks_depth] and one segment per cell (empty cells are
+    empty segments)."""
+    rng = np.random.default_rng(9)
+    pc, depth, feat, scale, (n_img, D, H, W_, C, n_cells) = _random_case(rng, "f16")
+    m = oracle.build_map(pc, n_img, D, H, W_, n_cells)
+    out = oracle.forward(depth, feat, "f16", scale, C, m, n_cells)
+    counts = np.bincount(m["ranks_bev"], minlength=n_cells)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    w = depth.reshape(-1)[m["ranks_depth"]]
+    seg = oracle.segment_reduce(w, feat.reshape(-1, C), "f16", scale, m["ranks_feat"], off)
+    assert np.array_equal(seg, out)
+
+
 ALL_CHECKS = [
     check_f16_decode_all_codes, check_e4m3_decode_all_codes,
     check_map_hand_example, check_map_vs_lexsort, check_map_invariants_on_workloads,
     check_forward_hand_example, check_forward_vs_dense, check_forward_closed_forms,
     check_forward_invariants, check_bad_cell_rejected,
+    check_segment_reduce_vs_embedding_bag, check_segment_reduce_is_bev_forward,
 ]

@@ -123,3 +123,26 @@ def test_baseline_rejects(lib):
     b = dict(a, fdt=dws.FP8_E4M3, C=40)                                  # 40-byte rows
     assert lib.bevpool_forward_baseline(0, *b.values()) == -2
     assert lib.bevpool_forward_baseline(1, *dict(a, out=None).values()) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(table=None), -1),
+    (dict(idx=None), -1),
+    (dict(off=None), -1),
+    (dict(out=None), -1),
+    (dict(n_seg=-1), -1),
+    (dict(C=0), -1),
+    (dict(tdt=dws.F16, wdt=dws.F32), -2),
+    (dict(C=12), -2),
+    (dict(n_seg=1 << 26, C=64), -3),
+    (dict(out=FAKE + 4), -1),
+])
+def test_segment_reduce_rejects(lib, kw, code):
+    a = dict(w=FAKE, wdt=dws.F16, table=FAKE, tdt=dws.F16, rows=10, C=80, scale=1.0, idx=FAKE,
+             off=FAKE, n_seg=4, n_pts=20, out=FAKE, stream=None)
+    a.update(kw)
+    assert lib.bevpool_segment_reduce(*a.values()) == code
+
+
+def test_segment_reduce_empty_is_noop(lib):
+    assert lib.bevpool_segment_reduce(None, 1, None, 1, 0, 8, 1.0, None, None, 0, 0, None, None) == 0

@@ -335,3 +335,59 @@ def test_baseline_orders_on_workloads(k, order):
     torch.cuda.synchronize()
     check_forward(out.cpu().numpy(), out_ref, out_abs, s.feat_dtype, ref["ranks_bev"],
                   f"baseline {order} workload {k}")
+
+
+
+# ------------------------------------------------- segmented gather-reduce
+def _gpu_segment_reduce(weights, table, scale, indices, offsets):
+    n_seg, C = offsets.size - 1, table.shape[-1]
+    out = torch.full((n_seg, C), float("nan"), dtype=torch.float32, device="cuda")
+    dws.bevpool_segment_reduce(to_gpu(weights) if weights is not None else None, to_gpu(table),
+                               to_gpu(indices), to_gpu(offsets), table_scale=scale, out=out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("k", [0, 1, 2, 3])
+def test_segment_reduce_on_bag_workloads(k):
+    b = W.make_bags(k)
+    s = b.spec
+    say(f"[bags {k} {s.name}] bags={s.n_bags} N={b.indices.size} C={s.C} {s.table_dtype}")
+    ref, ref_abs = oracle.segment_reduce(b.weights, b.table, s.table_dtype, b.table_scale,
+                                         b.indices, b.offsets, with_abs=True)
+    got = _gpu_segment_reduce(b.weights, b.table, b.table_scale, b.indices, b.offsets)
+    nonempty = np.nonzero(np.diff(b.offsets) > 0)[0]
+    check_forward(got, ref, ref_abs, s.table_dtype, nonempty, f"bags {k}")
+    again = _gpu_segment_reduce(b.weights, b.table, b.table_scale, b.indices, b.offsets)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32)), "not deterministic"
+
+
+@pytest.mark.parametrize("case", ["all_empty", "one_long", "lengths_around_split",
+                                  "unweighted_fp32", "leading_offset"])
+def test_segment_reduce_edge_cases(case):
+    rng = np.random.default_rng(33)
+    rows, C = 50, 80
+    table = rng.standard_normal((rows, C)).astype(np.float16)
+    if case == "all_empty":
+        lens = np.zeros(10, np.int64)
+    elif case == "one_long":
+        lens = np.array([3000])
+    elif case == "lengths_around_split":
+        lens = np.array([0, 1, 63, 64, 65, 95, 96, 97, 200, 0, 5])
+    else:
+        lens = rng.integers(0, 30, size=40)
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    idx = rng.integers(0, rows, size=max(int(off[-1]), 1)).astype(np.int32)
+    w = rng.random(idx.size).astype(np.float16)
+    dtype = "f16"
+    if case == "unweighted_fp32":
+        table, w, dtype = table.astype(np.float32), None, "f32"
+    if case == "leading_offset":                 # offsets need not start at 0
+        off = off + 7
+        idx = np.concatenate([rng.integers(0, rows, size=7).astype(np.int32), idx])
+        w = np.concatenate([rng.random(7).astype(np.float16), w])
+    say(f"[segment edge {case}] segments={off.size - 1} N={int(off[-1])}")
+    ref, ref_abs = oracle.segment_reduce(w, table, dtype, 1.0, idx, off, with_abs=True)
+    got = _gpu_segment_reduce(w, table, 1.0, idx, off)
+    nonempty = np.nonzero(np.diff(off) > 0)[0]
+    check_forward(got, ref, ref_abs, dtype, nonempty, case)

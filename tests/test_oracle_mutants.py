@@ -37,6 +37,12 @@ MUTANTS = [
      "double fscale = 1.0;"),
     ("first_point_kept_regardless", "if (point_cell[p] >= 0) { keys[k].cell",
      "if (point_cell[p] >= 0 || p == 0) { keys[k].cell"),
+    ("segment_skips_last_point", "for (int64_t t = offsets[s]; t < offsets[s + 1]; ++t) {",
+     "for (int64_t t = offsets[s]; t + 1 < offsets[s + 1]; ++t) {"),
+    ("segment_weight_ignored", "double w = weights ? load_value(weights, w_dtype, t) : 1.0;",
+     "double w = 1.0;"),
+    ("segment_row_is_point", "double term = w * (load_value(table, t_dtype, r * C + c) * tscale);",
+     "double term = w * (load_value(table, t_dtype, (t % n_rows) * C + c) * tscale);"),
 ]
 
 

@@ -40,7 +40,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["WorkloadSpec", "Workload", "SPECS", "spec", "make_workload",
-           "make_random_cells", "describe"]
+           "make_random_cells", "describe", "BagSpec", "BAG_SPECS", "make_bags"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -218,3 +218,65 @@ def describe(w: Workload) -> dict:
         "len_p99": float(np.percentile(occ, 99)) if occ.size else 0.0,
         "len_max": int(occ.max()) if occ.size else 0,
     }
+
+
+# ---------------------------------------------------------------------------
+# Weighted embedding bags: the segmented gather-reduce the BEV-pooling
+# article names as the same workload shape.  Inputs only, no arithmetic.
+@dataclasses.dataclass(frozen=True)
+class BagSpec:
+    name: str
+    n_bags: int
+    n_rows: int          # table rows
+    C: int
+    mean_len: float      # geometric bag lengths with this mean
+    empty_frac: float    # share of bags forced empty
+    n_long: int          # bags stretched to long_len (hot cells of a sparse workload)
+    long_len: int
+    table_dtype: str     # "f32" | "f16" | "e4m3"
+    weighted: bool = True
+
+
+BAG_SPECS = {
+    0: BagSpec("bags_tiny", 8, 20, 8, 3.0, 0.25, 1, 40, "f32"),
+    1: BagSpec("bags16k_c128_fp16", 16384, 262144, 128, 20.0, 0.05, 16, 1500, "f16"),
+    2: BagSpec("bags16k_c128_fp8", 16384, 262144, 128, 20.0, 0.05, 16, 1500, "e4m3"),
+    3: BagSpec("bags16k_c64_fp16_unweighted", 16384, 262144, 64, 20.0, 0.05, 16, 1500, "f16",
+               weighted=False),
+}
+
+
+@dataclasses.dataclass
+class Bags:
+    spec: BagSpec
+    table: np.ndarray        # [n_rows, C] float32 / float16 / uint8 e4m3 codes
+    table_scale: float
+    indices: np.ndarray      # int32 [N]
+    offsets: np.ndarray      # int32 [n_bags + 1]
+    weights: Optional[np.ndarray]   # [N] float32 / float16, or None
+
+
+def make_bags(k: int, seed: int = 0) -> Bags:
+    """rng draws: bag lengths (geometric), empty / long bag picks, row indices
+    (Zipf-like popularity: row = floor(n_rows * u**3)), weights U(0, 1), table
+    N(0, 1)."""
+    s = BAG_SPECS[k]
+    rng = np.random.default_rng(seed)
+    lens = rng.geometric(1.0 / s.mean_len, size=s.n_bags)
+    lens[rng.random(s.n_bags) < s.empty_frac] = 0
+    lens[rng.choice(s.n_bags, size=s.n_long, replace=False)] = s.long_len
+    offsets = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N = int(offsets[-1])
+    indices = np.minimum((s.n_rows * rng.random(N) ** 3).astype(np.int64), s.n_rows - 1)
+    weights = rng.random(N)
+    table = rng.standard_normal((s.n_rows, s.C))
+    scale = np.float32(1.0)
+    wdt = np.float32 if s.table_dtype == "f32" else np.float16
+    if s.table_dtype == "f32":
+        table = table.astype(np.float32)
+    elif s.table_dtype == "f16":
+        table = table.astype(np.float16)
+    else:
+        table, scale = quantize_e4m3(table.astype(np.float16).astype(np.float64))
+    return Bags(s, np.ascontiguousarray(table), float(scale), indices.astype(np.int32), offsets,
+                weights.astype(wdt) if s.weighted else None)
