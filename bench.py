@@ -51,6 +51,8 @@ def parse():
                     help="benchmark bevpool_segment_reduce on embedding-bag workload k instead")
     ap.add_argument("--kernel", choices=["owned", "v2", "v2do"], default="owned",
                     help="owned: bevpool_forward; v2 / v2do: the tile-outer / depth-outer baselines")
+    ap.add_argument("--out-dtype", choices=["f32", "f16", "bf16"], default="f32",
+                    help="output type of the owned kernel (f16/bf16 via bevpool_forward_ex)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-oracle sample length")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -64,12 +66,12 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(spec, N, I):
+def algorithmic_bytes(spec, N, I, out_bytes=4):
     per_point = spec.C * ELEM_BYTES[spec.feat_dtype] + ELEM_BYTES[spec.depth_dtype] + 12
-    b_alg = N * per_point + 8 * I + spec.n_cells * spec.C * 4
+    b_alg = N * per_point + 8 * I + spec.n_cells * spec.C * out_bytes
     b_min = (spec.n_feat_rows * spec.C * ELEM_BYTES[spec.feat_dtype]
              + spec.n_img * spec.D * spec.H * spec.W * ELEM_BYTES[spec.depth_dtype]
-             + 12 * N + 8 * I + spec.n_cells * spec.C * 4)
+             + 12 * N + 8 * I + spec.n_cells * spec.C * out_bytes)
     return b_alg, b_min
 
 
@@ -138,6 +140,11 @@ def summarize(args):
     if fwd_fetch is not None and fwd_write is not None and f_scale and w_scale:
         traffic = int(round((fwd_fetch * f_scale + fwd_write * w_scale) * 1024))
     avg_ns = float(fwd[0]["AverageNs"]) if fwd else None
+    # per-dispatch durations of the forward kernel from the same trace
+    durs = sorted(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                  for r in _read_csv(trace_dir, "kernel_trace.csv") if "bev_pool_fwd" in r["Kernel_Name"])
+    med_ns = durs[len(durs) // 2] if durs else None
+    p10_ns = durs[len(durs) // 10] if durs else None
     name = "bev_pool_fwd"
     lines = [f"# {name} on {workload} (MI355X, gfx950)", "",
              "Commands (from the repository root):", "", "```", args.commands.strip(), "```", "",
@@ -149,6 +156,9 @@ def summarize(args):
     lines += ["", "## Benchmark line (same build)", "",
               f"- per call (HIP events, graph replay): {bench['us_per_call']} us",
               f"- rocprof average kernel duration: {avg_ns / 1e3:.3f} us" if avg_ns else "- rocprof: n/a",
+              f"- rocprof per-dispatch median {med_ns / 1e3:.3f} us, 10th percentile "
+              f"{p10_ns / 1e3:.3f} us over {len(durs)} dispatches (start-to-end timestamps, "
+              f"which include each dispatch's completion signal under tracing)" if durs else "",
               f"- algorithmic bytes per call: {bench['bytes']['algorithmic']}",
               f"- effective bandwidth: {bench['value']} GB/s ({bench['pct_hbm_peak']} % of 8 TB/s)", "",
               "## HBM traffic (rocprofv3 --pmc, one counter per run, KiB per dispatch)", "",
@@ -169,15 +179,19 @@ def summarize(args):
                      "hbm_bytes_per_launch": traffic, "fetch_kib": fwd_fetch, "write_kib": fwd_write,
                      "copy_calibration": {"kib": copy_kib, "fetch_kib": copy_fetch,
                                           "write_kib": copy_write},
-                     "rocprof_avg_ns": avg_ns}
+                     "rocprof_avg_ns": avg_ns, "rocprof_median_ns": med_ns}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
     print(f"wrote {out_md} and {TRAFFIC_FILE}")
 
 
-def cpu_baseline(wl, ref_map, b_alg, seconds):
+def cpu_baseline(wl, b_alg, seconds):
+    """The oracle's scatter-reduce timed on the host, on a map it builds
+    itself from the same seeded geometry."""
     import oracle
+    oracle.build(force=False)
     s = wl.spec
+    ref_map = oracle.build_map(wl.point_cell, s.n_img, s.D, s.H, s.W, s.n_cells)
     reps, t0 = 0, time.perf_counter()
     while True:
         oracle.forward(wl.depth, wl.feat, s.feat_dtype, wl.feat_scale, s.C, ref_map, s.n_cells)
@@ -243,10 +257,10 @@ def bench_bags(args):
         "metric": "bevpool_segment_reduce µs/call + effective GB/s (% HBM peak), weighted embedding bags",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": f"{s.table_dtype} table, f32 accumulate/out",
+        "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (geometric bag lengths, skewed rows, N(0,1) table)",
         "config": {"workload": s.name, "bags": s.n_bags, "points": N, "table_rows": s.n_rows,
-                   "C": s.C, "weighted": w is not None},
+                   "C": s.C, "table_dtype": s.table_dtype, "weighted": w is not None},
         "us_per_call": round(ms * 1e3, 3), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
@@ -264,6 +278,9 @@ def main():
             sys.exit(2)
         bench_bags(args)
         return
+    if args.out_dtype != "f32" and args.kernel != "owned":
+        print("--out-dtype applies to the owned kernel only", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the pooled forward has no cross-GPU step in "
               f"this build (asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -285,22 +302,27 @@ def main():
     point_cell = torch.from_numpy(wl.point_cell).to(dev)
     depth = torch.from_numpy(wl.depth).to(dev)
     feat = torch.from_numpy(wl.feat).to(dev)
-    out = torch.empty((s.n_cells, s.C), dtype=torch.float32, device=dev)
+    out_torch = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[args.out_dtype]
+    out = torch.empty((s.n_cells, s.C), dtype=out_torch, device=dev)
     m = dws.bevpool_build_map(point_cell, s.n_img, s.D, s.H, s.W, s.n_cells)   # warm
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     m = dws.bevpool_build_map(point_cell, s.n_img, s.D, s.H, s.W, s.n_cells)
     map_ms = (time.perf_counter() - t0) * 1e3
     N, I = m.n_points, m.n_intervals
-    b_alg, b_min = algorithmic_bytes(s, N, I)
+    b_alg, b_min = algorithmic_bytes(s, N, I, out.element_size())
 
     lib = dws._load()
     stream = torch.cuda.current_stream()
-    fargs = dws.forward_args(depth, feat, m, s.n_cells, out, wl.feat_scale, stream)
+    narrow = args.out_dtype != "f32"
+    make_args = dws.forward_ex_args if narrow else dws.forward_args
+    fargs = make_args(depth, feat, m, s.n_cells, out, wl.feat_scale, stream)
 
     order = {"v2": dws.ORDER_TILE_OUTER, "v2do": dws.ORDER_DEPTH_OUTER}.get(args.kernel)
 
     def call(a):
+        if narrow:
+            return lib.bevpool_forward_ex(*a)
         if order is None:
             return lib.bevpool_forward(*a)
         return lib.bevpool_forward_baseline(order, *a)
@@ -323,7 +345,7 @@ def main():
         cap_stream = torch.cuda.Stream()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=cap_stream):
-            gargs = dws.forward_args(depth, feat, m, s.n_cells, out, wl.feat_scale, cap_stream)
+            gargs = make_args(depth, feat, m, s.n_cells, out, wl.feat_scale, cap_stream)
             for _ in range(chunk):
                 rc = call(gargs)
                 if rc != 0:
@@ -397,7 +419,8 @@ def main():
             torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
 
-    traffic = traffic_for(s.name)
+    workload_key = s.name if not narrow else f"{s.name}_out_{args.out_dtype}"
+    traffic = traffic_for(workload_key)
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -409,13 +432,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f16": "f16 in, f32 accumulate/out", "f32": "f32",
-                  "e4m3": "e4m3 in, f32 accumulate/out"}[s.feat_dtype],
+        "dtype": "f32",     # accumulation type; storage types are in config
         "data": "synthetic (seeded camera-frustum geometry; N(0,1) features, softmax depth)",
-        "config": {"workload": s.name, "cameras": s.n_cam, "frames": s.frames, "D": s.D,
+        "config": {"workload": workload_key, "cameras": s.n_cam, "frames": s.frames, "D": s.D,
                    "H": s.H, "W": s.W, "C": s.C, "bev_grid": [s.frames, s.G, s.G],
                    "scatter_points": N, "intervals": I, "feat_dtype": s.feat_dtype,
-                   "depth_dtype": s.depth_dtype, "kernel": args.kernel,
+                   "depth_dtype": s.depth_dtype, "out_dtype": args.out_dtype,
+                   "kernel": args.kernel,
                    "timing": "eager" if graph is None else
                    f"hip graph replay, {chunk} calls per graph"},
         "us_per_call": round(us, 3),
@@ -438,11 +461,7 @@ def main():
                       "kernel_sha256_16": kernel_hash()},
     }
     if not args.no_cpu:
-        import oracle
-        ref_map = {"ranks_depth": m.ranks_depth.cpu().numpy(), "ranks_feat": m.ranks_feat.cpu().numpy(),
-                   "ranks_bev": m.ranks_bev.cpu().numpy(), "n_points": N}
-        oracle.build(force=False)
-        result["cpu_baseline"] = cpu_baseline(wl, ref_map, b_alg, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, b_alg, args.cpu_seconds)
     if args.details:
         with open(args.details, "w") as f:
             json.dump(result, f, indent=1)

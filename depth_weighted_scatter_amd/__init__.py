@@ -18,18 +18,20 @@ import torch
 __all__ = ["BevPoolError", "BevMap", "F32", "F16", "FP8_E4M3", "library_path",
            "bevpool_status_string", "bevpool_version", "bevpool_build_map_workspace_size",
            "bevpool_build_map", "bevpool_forward", "bevpool_forward_baseline", "forward_args",
+           "bevpool_forward_ex", "forward_ex_args", "BF16",
            "bevpool_segment_reduce", "segment_reduce_args",
            "ORDER_TILE_OUTER", "ORDER_DEPTH_OUTER"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libbevpool.so")
 
-F32, F16, FP8_E4M3 = 0, 1, 2
+F32, F16, FP8_E4M3, BF16 = 0, 1, 2, 3
 ORDER_TILE_OUTER, ORDER_DEPTH_OUTER = 0, 1
 OK, ERR_CAPACITY = 0, -5
 
 _TORCH_DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.uint8: FP8_E4M3,
                      torch.float8_e4m3fn: FP8_E4M3}
+_OUT_DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 
 
 class BevPoolError(RuntimeError):
@@ -68,6 +70,9 @@ def _load():
     lib.bevpool_forward.restype = ctypes.c_int
     lib.bevpool_forward.argtypes = [vp, i32, i64, vp, i32, i64, i32, ctypes.c_float,
                                     vp, vp, vp, vp, vp, i32, i32, vp, i64, vp]
+    lib.bevpool_forward_ex.restype = ctypes.c_int
+    lib.bevpool_forward_ex.argtypes = [vp, i32, i64, vp, i32, i64, i32, ctypes.c_float,
+                                       vp, vp, vp, vp, vp, i32, i32, vp, i32, i64, vp]
     lib.bevpool_forward_baseline.restype = ctypes.c_int
     lib.bevpool_forward_baseline.argtypes = [i32] + lib.bevpool_forward.argtypes
     lib.bevpool_segment_reduce.restype = ctypes.c_int
@@ -147,16 +152,13 @@ def bevpool_build_map(point_cell: torch.Tensor, n_img: int, D: int, H: int, W: i
     return BevMap(arrs[0][:N], arrs[1][:N], arrs[2][:N], arrs[3][:I], arrs[4][:I], N, I)
 
 
-def forward_args(depth: torch.Tensor, feat: torch.Tensor, m: BevMap, n_cells: int,
-                 out: torch.Tensor, feat_scale: float = 1.0, stream=None) -> tuple:
-    """Validated, marshalled argument tuple for the C bevpool_forward.
-
-    Lets a caller that launches many times (a benchmark, a graph capture)
-    pay the Python-side checks once: _load().bevpool_forward(*args).
-    """
+def _forward_inputs(depth: torch.Tensor, feat: torch.Tensor, m: BevMap, n_cells: int,
+                    out: torch.Tensor, feat_scale: float) -> tuple:
+    # Checks shared by the forward entry points; returns the C arguments up
+    # to n_intervals (out, its type, n_cells and the stream follow).
     _check_device_tensor("depth", depth)
     _check_device_tensor("feat", feat)
-    _check_device_tensor("out", out, torch.float32)
+    _check_device_tensor("out", out)
     if depth.dtype not in (torch.float32, torch.float16):
         raise TypeError(f"depth must be float32 or float16, got {depth.dtype}")
     if feat.dtype not in _TORCH_DTYPE_CODE:
@@ -169,7 +171,29 @@ def forward_args(depth: torch.Tensor, feat: torch.Tensor, m: BevMap, n_cells: in
             float(feat_scale),
             m.ranks_depth.data_ptr(), m.ranks_feat.data_ptr(), m.ranks_bev.data_ptr(),
             m.interval_starts.data_ptr(), m.interval_lengths.data_ptr(),
-            m.n_points, m.n_intervals, out.data_ptr(), n_cells, _stream_ptr(stream))
+            m.n_points, m.n_intervals)
+
+
+def forward_args(depth: torch.Tensor, feat: torch.Tensor, m: BevMap, n_cells: int,
+                 out: torch.Tensor, feat_scale: float = 1.0, stream=None) -> tuple:
+    """Validated, marshalled argument tuple for the C bevpool_forward.
+
+    Lets a caller that launches many times (a benchmark, a graph capture)
+    pay the Python-side checks once: _load().bevpool_forward(*args).
+    """
+    _check_device_tensor("out", out, torch.float32)
+    return _forward_inputs(depth, feat, m, n_cells, out, feat_scale) + (
+        out.data_ptr(), n_cells, _stream_ptr(stream))
+
+
+def forward_ex_args(depth: torch.Tensor, feat: torch.Tensor, m: BevMap, n_cells: int,
+                    out: torch.Tensor, feat_scale: float = 1.0, stream=None) -> tuple:
+    """Marshalled argument tuple for the C bevpool_forward_ex; the output
+    type (float32, float16 or bfloat16) is out's dtype."""
+    if out.dtype not in _OUT_DTYPE_CODE:
+        raise TypeError(f"out must be float32, float16 or bfloat16, got {out.dtype}")
+    return _forward_inputs(depth, feat, m, n_cells, out, feat_scale) + (
+        out.data_ptr(), _OUT_DTYPE_CODE[out.dtype], n_cells, _stream_ptr(stream))
 
 
 def bevpool_forward(depth: torch.Tensor, feat: torch.Tensor, m: BevMap, n_cells: int,
@@ -187,6 +211,21 @@ def bevpool_forward(depth: torch.Tensor, feat: torch.Tensor, m: BevMap, n_cells:
     rc = lib.bevpool_forward(*forward_args(depth, feat, m, n_cells, out, feat_scale, stream))
     if rc != OK:
         raise BevPoolError("bevpool_forward", rc)
+    return out
+
+
+def bevpool_forward_ex(depth: torch.Tensor, feat: torch.Tensor, m: BevMap, n_cells: int,
+                       out_dtype: torch.dtype = torch.float16, feat_scale: float = 1.0,
+                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """bevpool_forward with the fp32 sums rounded (nearest-even) to out_dtype
+    (float32, float16 or bfloat16) at the store; returns out [n_cells, C]."""
+    lib = _load()
+    if out is None:
+        out = torch.empty((n_cells, feat.shape[-1]), dtype=out_dtype, device=feat.device)
+    rc = lib.bevpool_forward_ex(*forward_ex_args(depth, feat, m, n_cells, out, feat_scale,
+                                                 stream))
+    if rc != OK:
+        raise BevPoolError("bevpool_forward_ex", rc)
     return out
 
 

@@ -90,7 +90,8 @@ __global__ __launch_bounds__(kBlock) void baseline_scatter(FwdParams p, int tile
         tile_fma<FT>(acc, d, feat[p.ranks_feat[t] * tiles + tile]);
     }
     const float scale = FT == kE4M3 ? p.feat_scale : 1.f;
-    f32x4 *o = reinterpret_cast<f32x4 *>(p.out + int64_t(p.ranks_bev[start]) * p.C + tile * E);
+    f32x4 *o = reinterpret_cast<f32x4 *>(static_cast<float *>(p.out) +
+                                         int64_t(p.ranks_bev[start]) * p.C + tile * E);
 #pragma unroll
     for (int e = 0; e < E; e += 4)
         o[e / 4] = f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]} * scale;

@@ -19,7 +19,7 @@ int elem_bytes(int32_t dtype)
     case BEVPOOL_F32: return 4;
     case BEVPOOL_F16: return 2;
     case BEVPOOL_FP8_E4M3: return 1;
-    default: return 0;
+    default: return 0;   // bf16 is an output type only
     }
 }
 
@@ -105,8 +105,11 @@ int validate_forward(const void *depth, int32_t depth_dtype, int64_t n_depth, co
                      const int32_t *ranks_depth, const int32_t *ranks_feat,
                      const int32_t *ranks_bev, const int32_t *interval_starts,
                      const int32_t *interval_lengths, int32_t n_points, int32_t n_intervals,
-                     float *out, int64_t n_cells, bool tiles16, bevpool::FwdParams &p)
+                     void *out, int32_t out_dtype, int64_t n_cells, bool tiles16,
+                     bevpool::FwdParams &p)
 {
+    if (out_dtype != BEVPOOL_F32 && out_dtype != BEVPOOL_F16 && out_dtype != BEVPOOL_BF16)
+        return BEVPOOL_ERR_UNSUPPORTED;
     if (!out || n_cells <= 0 || C <= 0 || n_points < 0 || n_intervals < 0 ||
         n_intervals > n_points)
         return BEVPOOL_ERR_INVALID_ARG;
@@ -128,7 +131,7 @@ int validate_forward(const void *depth, int32_t depth_dtype, int64_t n_depth, co
 
     if (n_cells * C > kInt32Limit || n_feat_rows * C > kInt32Limit || n_depth > kInt32Limit)
         return BEVPOOL_ERR_OVERFLOW;
-    if (!aligned(out, 16) || (feat && !aligned(feat, 16)) ||
+    if (!aligned(out, out_dtype == BEVPOOL_F32 ? 16 : 8) || (feat && !aligned(feat, 16)) ||
         (depth && !aligned(depth, uintptr_t(elem_bytes(depth_dtype)))))
         return BEVPOOL_ERR_INVALID_ARG;
 
@@ -145,6 +148,7 @@ int validate_forward(const void *depth, int32_t depth_dtype, int64_t n_depth, co
     p.interval_lengths = interval_lengths;
     p.n_intervals = n_intervals;
     p.out = out;
+    p.out_dtype = out_dtype;
     p.n_cells = int32_t(n_cells);
     p.depth_dtype = depth_dtype;
     p.feat_dtype = feat_dtype;
@@ -155,6 +159,24 @@ int validate_forward(const void *depth, int32_t depth_dtype, int64_t n_depth, co
 
 extern "C" {
 
+int bevpool_forward_ex(const void *depth, int32_t depth_dtype, int64_t n_depth,
+                       const void *feat, int32_t feat_dtype, int64_t n_feat_rows, int32_t C,
+                       float feat_scale,
+                       const int32_t *ranks_depth, const int32_t *ranks_feat,
+                       const int32_t *ranks_bev,
+                       const int32_t *interval_starts, const int32_t *interval_lengths,
+                       int32_t n_points, int32_t n_intervals,
+                       void *out, int32_t out_dtype, int64_t n_cells, hipStream_t stream)
+{
+    bevpool::FwdParams p;
+    const int st = validate_forward(depth, depth_dtype, n_depth, feat, feat_dtype, n_feat_rows, C,
+                                    feat_scale, ranks_depth, ranks_feat, ranks_bev,
+                                    interval_starts, interval_lengths, n_points, n_intervals,
+                                    out, out_dtype, n_cells, false, p);
+    if (st != BEVPOOL_OK) return st;
+    return bevpool::run_forward(p, stream) == hipSuccess ? BEVPOOL_OK : BEVPOOL_ERR_HIP;
+}
+
 int bevpool_forward(const void *depth, int32_t depth_dtype, int64_t n_depth,
                     const void *feat, int32_t feat_dtype, int64_t n_feat_rows, int32_t C,
                     float feat_scale,
@@ -164,13 +186,10 @@ int bevpool_forward(const void *depth, int32_t depth_dtype, int64_t n_depth,
                     int32_t n_points, int32_t n_intervals,
                     float *out, int64_t n_cells, hipStream_t stream)
 {
-    bevpool::FwdParams p;
-    const int st = validate_forward(depth, depth_dtype, n_depth, feat, feat_dtype, n_feat_rows, C,
-                                    feat_scale, ranks_depth, ranks_feat, ranks_bev,
-                                    interval_starts, interval_lengths, n_points, n_intervals,
-                                    out, n_cells, false, p);
-    if (st != BEVPOOL_OK) return st;
-    return bevpool::run_forward(p, stream) == hipSuccess ? BEVPOOL_OK : BEVPOOL_ERR_HIP;
+    return bevpool_forward_ex(depth, depth_dtype, n_depth, feat, feat_dtype, n_feat_rows, C,
+                              feat_scale, ranks_depth, ranks_feat, ranks_bev, interval_starts,
+                              interval_lengths, n_points, n_intervals, out, BEVPOOL_F32, n_cells,
+                              stream);
 }
 
 int bevpool_forward_baseline(int32_t order, const void *depth, int32_t depth_dtype,
@@ -188,7 +207,7 @@ int bevpool_forward_baseline(int32_t order, const void *depth, int32_t depth_dty
     const int st = validate_forward(depth, depth_dtype, n_depth, feat, feat_dtype, n_feat_rows, C,
                                     feat_scale, ranks_depth, ranks_feat, ranks_bev,
                                     interval_starts, interval_lengths, n_points, n_intervals,
-                                    out, n_cells, true, p);
+                                    out, BEVPOOL_F32, n_cells, true, p);
     if (st != BEVPOOL_OK) return st;
     return bevpool::run_forward_baseline(p, order == BEVPOOL_ORDER_TILE_OUTER, stream) ==
                    hipSuccess
@@ -228,6 +247,7 @@ int bevpool_segment_reduce(const void *weights, int32_t weight_dtype, const void
     p.interval_starts = offsets;
     p.n_intervals = n_segments;
     p.out = out;
+    p.out_dtype = bevpool::kF32;
     p.n_cells = n_segments;
     p.depth_dtype = weight_dtype;
     p.feat_dtype = table_dtype;

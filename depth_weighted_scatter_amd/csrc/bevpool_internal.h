@@ -29,7 +29,7 @@ size_t map_workspace_bytes(int64_t P);
 hipError_t run_build_map(const MapParams &p, int32_t h_counts[3], hipStream_t stream);
 
 // ---- forward -----------------------------------------------------------------
-enum DType : int32_t { kF32 = 0, kF16 = 1, kE4M3 = 2 };
+enum DType : int32_t { kF32 = 0, kF16 = 1, kE4M3 = 2, kBF16 = 3 };
 
 struct FwdParams {
     const void *depth;
@@ -40,7 +40,8 @@ struct FwdParams {
     const int32_t *ranks_depth, *ranks_feat, *ranks_bev, *interval_starts, *interval_lengths;
     int32_t n_intervals;
     int32_t n_long_blocks;       // blocks in the long-interval role (set by run_forward)
-    float *out;                  // [n_cells, C], 16-byte aligned
+    void *out;                   // [n_cells, C] of out_dtype, 16-byte aligned
+    int32_t out_dtype;           // kF32, kF16 or kBF16
     int32_t n_cells;
     int32_t depth_dtype, feat_dtype;
 };

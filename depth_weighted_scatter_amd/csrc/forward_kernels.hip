@@ -54,6 +54,7 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
@@ -62,8 +63,6 @@ constexpr int kBlock = kWave * kWavesPerBlock;
 constexpr int kShortMax = 96;   // longest interval a single wave owns
 constexpr int kRoundPoints = 18; // points per row-request round of a wave
 constexpr int kLongScan = 16;    // intervals scanned per long-interval block
-
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // A lane's share of a feature row: CB bytes (16, or 8 for e4m3 rows up to
 // 512 bytes, which keeps e4m3 on the same ten-lane row geometry as fp16).
@@ -110,15 +109,44 @@ template <int CB> struct Accum<kE4M3, CB> {
     }
 };
 
+// Stores output elements 4q .. 4q+3 (a float4 of the row-major [cells, C]
+// output) in the output type, non-temporally.  The 16-bit conversions round
+// to nearest-even (gfx950 converts fp32 pairs to bf16 natively).
+__device__ inline void store4(void *out, int out_dtype, int q, f32x4 v)
+{
+    if (out_dtype == kF32) {
+        __builtin_nontemporal_store(v, static_cast<f32x4 *>(out) + q);
+        return;
+    }
+    u32x2 w;
+    if (out_dtype == kF16) {
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        w[0] = __builtin_bit_cast(uint32_t, f16x2{static_cast<_Float16>(v[0]), static_cast<_Float16>(v[1])});
+        w[1] = __builtin_bit_cast(uint32_t, f16x2{static_cast<_Float16>(v[2]), static_cast<_Float16>(v[3])});
+    } else {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        w[0] = __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1])});
+        w[1] = __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])});
+    }
+    __builtin_nontemporal_store(w, static_cast<u32x2 *>(out) + q);
+}
+
 // Zeroes cells [cell_lo, cell_hi) of out with non-temporal stores; `lane`
 // and `lanes` give this thread's position among the cooperating threads.
-__device__ inline void zero_cells(float *out, int C, int cell_lo, int cell_hi, int lane, int lanes)
+__device__ inline void zero_cells(void *out, int out_dtype, int C, int cell_lo, int cell_hi,
+                                  int lane, int lanes)
 {
     if (cell_hi <= cell_lo) return;
-    f32x4 *o = reinterpret_cast<f32x4 *>(out);
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     const int q0 = cell_lo * (C / 4), q1 = cell_hi * (C / 4);
-    for (int q = q0 + lane; q < q1; q += lanes) __builtin_nontemporal_store(z, o + q);
+    if (out_dtype == kF32) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        for (int q = q0 + lane; q < q1; q += lanes)
+            __builtin_nontemporal_store(z, static_cast<f32x4 *>(out) + q);
+    } else {
+        const u32x2 z = {0u, 0u};
+        for (int q = q0 + lane; q < q1; q += lanes)
+            __builtin_nontemporal_store(z, static_cast<u32x2 *>(out) + q);
+    }
 }
 
 // Lane i reads the map indices of point t0 + min(i, n - 1), 1 <= n <= 64:
@@ -249,7 +277,7 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
     s.lane = lane;
     s.ok = s.g < s.PPW;
     const float scale = FT == kE4M3 ? p.feat_scale : 1.f;
-    f32x4 *o = reinterpret_cast<f32x4 *>(p.out);
+    const int od = p.out_dtype;
     float acc[E];
 
     if (int(blockIdx.x) >= p.n_long_blocks) {
@@ -267,11 +295,11 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
         const int bev = __builtin_amdgcn_readlane(cells, 1);
         fold_slots<E>(red[wv], acc, s, C, [&](int q, f32x4 sum) {
             if (FT == kE4M3) sum *= scale;
-            __builtin_nontemporal_store(sum, o + bev * C4 + q);
+            store4(p.out, od, bev * C4 + q, sum);
         });
         const int prev_bev = iv > 0 ? __builtin_amdgcn_readlane(cells, 0) : -1;
-        zero_cells(p.out, C, prev_bev + 1, bev, lane, kWave);
-        if (iv == p.n_intervals - 1) zero_cells(p.out, C, bev + 1, p.n_cells, lane, kWave);
+        zero_cells(p.out, od, C, prev_bev + 1, bev, lane, kWave);
+        if (iv == p.n_intervals - 1) zero_cells(p.out, od, C, bev + 1, p.n_cells, lane, kWave);
         return;
     }
 
@@ -308,20 +336,21 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
                 for (int w = 1; w < kWavesPerBlock; ++w)
                     sum += *reinterpret_cast<const f32x4 *>(part + w * C + 4 * q);
                 if (FT == kE4M3) sum *= scale;
-                __builtin_nontemporal_store(sum, o + bev * C4 + q);
+                store4(p.out, od, bev * C4 + q, sum);
             }
-            zero_cells(p.out, C, prev_bev + 1, bev, threadIdx.x, kBlock);
-            if (iv == p.n_intervals - 1) zero_cells(p.out, C, bev + 1, p.n_cells, threadIdx.x, kBlock);
+            zero_cells(p.out, od, C, prev_bev + 1, bev, threadIdx.x, kBlock);
+            if (iv == p.n_intervals - 1)
+                zero_cells(p.out, od, C, bev + 1, p.n_cells, threadIdx.x, kBlock);
             __syncthreads();                                // part is reused
         }
     }
 }
 
-__global__ __launch_bounds__(kBlock) void zero_fill(f32x4 *out, int n4)
+__global__ __launch_bounds__(kBlock) void zero_fill(void *out, int out_dtype, int n4)
 {
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     for (int i = blockIdx.x * kBlock + threadIdx.x; i < n4; i += gridDim.x * kBlock)
-        __builtin_nontemporal_store(z, out + i);
+        store4(out, out_dtype, i, z);
 }
 
 template <int DT, int FT, int CB, bool SEG>
@@ -373,7 +402,7 @@ hipError_t run_forward(const FwdParams &p, hipStream_t s)
     if (p.n_intervals == 0) {
         const int n4 = p.n_cells * (p.C / 4);
         const int blocks = min((n4 + kBlock - 1) / kBlock, 4096);
-        zero_fill<<<blocks, kBlock, 0, s>>>(reinterpret_cast<f32x4 *>(p.out), n4);
+        zero_fill<<<blocks, kBlock, 0, s>>>(p.out, p.out_dtype, n4);
         return hipGetLastError();
     }
     return dispatch<false>(p, s);

@@ -57,7 +57,8 @@ typedef enum bevpool_status {
 typedef enum bevpool_dtype {
     BEVPOOL_F32 = 0,
     BEVPOOL_F16 = 1,
-    BEVPOOL_FP8_E4M3 = 2
+    BEVPOOL_FP8_E4M3 = 2,
+    BEVPOOL_BF16 = 3   /* output type of bevpool_forward_ex only */
 } bevpool_dtype;
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -151,6 +152,34 @@ int bevpool_forward(const void *depth, int32_t depth_dtype, int64_t n_depth,
                     const int32_t *interval_starts, const int32_t *interval_lengths,
                     int32_t n_points, int32_t n_intervals,
                     float *out, int64_t n_cells, hipStream_t stream);
+
+/*
+ * bevpool_forward_ex -- bevpool_forward with a choice of output type, for
+ * callers whose output traffic is the larger share of a DRAM-bound call.
+ * The article's FP8 path halves the output bytes as well as the feature bytes
+ * (Figure 4, and the section on classifying the memory regime: when the
+ * working set spills out of L2, fewer bytes is the target).
+ *
+ * Accumulation stays fp32 in registers; each finished fp32 sum is rounded
+ * once, to nearest-even, to out_dtype at the store:
+ *   out_dtype BEVPOOL_F32  -- identical to bevpool_forward;
+ *   out_dtype BEVPOOL_F16  -- IEEE binary16 (sums beyond 65504 become inf);
+ *   out_dtype BEVPOOL_BF16 -- bfloat16 (fp32's exponent range, 8-bit
+ *                             significand).
+ *   out [n_cells, C] of out_dtype (device; 16-byte aligned for F32, 8-byte
+ *       aligned for F16/BF16), overwritten, empty cells 0.
+ * Every other argument, the supported combinations and the behaviour are
+ * those of bevpool_forward.  Errors: as bevpool_forward; UNSUPPORTED for an
+ * out_dtype other than the three above.
+ */
+int bevpool_forward_ex(const void *depth, int32_t depth_dtype, int64_t n_depth,
+                       const void *feat, int32_t feat_dtype, int64_t n_feat_rows, int32_t C,
+                       float feat_scale,
+                       const int32_t *ranks_depth, const int32_t *ranks_feat,
+                       const int32_t *ranks_bev,
+                       const int32_t *interval_starts, const int32_t *interval_lengths,
+                       int32_t n_points, int32_t n_intervals,
+                       void *out, int32_t out_dtype, int64_t n_cells, hipStream_t stream);
 
 /*
  * bevpool_segment_reduce -- the interval-owned kernel applied to a generic

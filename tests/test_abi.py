@@ -90,6 +90,30 @@ def test_forward_rejects(lib, kw, code):
     assert _fwd(lib, **kw) == code
 
 
+def _fwd_ex(lib, **kw):
+    a = dict(depth=FAKE, ddt=dws.F16, n_depth=100, feat=FAKE, fdt=dws.F16, rows=10, C=80,
+             scale=1.0, rd=FAKE, rf=FAKE, rb=FAKE, st=FAKE, ln=FAKE, n_points=5, n_iv=2,
+             out=FAKE, odt=dws.F16, n_cells=16, stream=None)
+    a.update(kw)
+    return lib.bevpool_forward_ex(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(odt=dws.FP8_E4M3), -2),               # e4m3 is not an output type
+    (dict(odt=4), -2),
+    (dict(odt=-1), -2),
+    (dict(out=None), -1),
+    (dict(out=FAKE + 4), -1),                   # 16-bit output must be 8-byte aligned
+    (dict(odt=dws.BF16, out=FAKE + 2), -1),
+    (dict(odt=dws.F32, out=FAKE + 8), -1),      # fp32 output must be 16-byte aligned
+    (dict(ddt=dws.F32), -2),                    # input checks are bevpool_forward's
+    (dict(C=12), -2),
+    (dict(n_cells=1 << 26, C=64), -3),
+])
+def test_forward_ex_rejects(lib, kw, code):
+    assert _fwd_ex(lib, **kw) == code
+
+
 def _map(lib, **kw):
     n_pts, n_iv = ctypes.c_int32(), ctypes.c_int32()
     a = dict(pc=FAKE, n_img=1, D=2, H=2, W=2, n_cells=4, rd=FAKE, rf=FAKE, rb=FAKE, st=FAKE,
