@@ -153,13 +153,16 @@ __device__ inline void zero_cells(void *out, int out_dtype, int C, int cell_lo, 
 // lanes past the batch repeat its last point, so every address derived from
 // them stays in bounds and no lane needs an exec-masked branch.
 // In segment mode (SEG) the weight of point t is read directly at t.
+// These are ordinary (cached) loads: the map is reused by every call for the
+// same geometry, and streaming loads that keep it out of the caches measured
+// 3-21% slower (the larger figure on the 1.6M-point batched workload).
 template <bool SEG>
 __device__ inline void load_indices(const FwdParams &p, int t0, int n, int lane, int &row,
                                     int &didx)
 {
     const int t = t0 + min(lane, n - 1);
-    row = __builtin_nontemporal_load(p.ranks_feat + t);
-    didx = SEG ? t : __builtin_nontemporal_load(p.ranks_depth + t);
+    row = p.ranks_feat[t];
+    didx = SEG ? t : p.ranks_depth[t];
 }
 
 // Lane geometry of a wave: lane (g, k) = g*G + k holds chunk k of slot g.
@@ -260,9 +263,13 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
     constexpr int E = CB / elem_bytes(FT);   // row elements per lane
     constexpr int PPW_CT = G_CT > 0 ? kWave / G_CT : 1;
     // rows in flight per lane: about kRoundPoints points per request round,
-    // which keeps the common kernels near 64 VGPRs (up to eight waves per SIMD)
+    // which keeps the common kernels near 64 VGPRs (up to eight waves per SIMD);
+    // rows of 16 or more chunks (at most four points per instruction) take
+    // four instructions per round, which measured faster than more rows in
+    // flight at half the occupancy (C = 128 and 256)
     constexpr int SUB_RAW = G_CT > 0 ? (kRoundPoints + PPW_CT - 1) / PPW_CT : 4;
-    constexpr int SUB = SUB_RAW > 8 ? 8 : (SUB_RAW > 5 && E == 16 ? 5 : SUB_RAW);
+    constexpr int SUB = G_CT >= 16 ? (SUB_RAW > 4 ? 4 : SUB_RAW)
+                                   : SUB_RAW > 8 ? 8 : (SUB_RAW > 5 && E == 16 ? 5 : SUB_RAW);
     __shared__ __attribute__((aligned(16))) float red[kWavesPerBlock][kWave * E];
     extern __shared__ __attribute__((aligned(16))) float part[];   // [kWavesPerBlock][C]
 
