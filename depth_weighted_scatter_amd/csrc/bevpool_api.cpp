@@ -10,6 +10,8 @@
 namespace {
 
 constexpr int64_t kInt32Limit = int64_t(INT32_MAX);   // sizes must stay below 2^31
+// Feature rows are addressed as a table base plus a 32-bit unsigned byte offset.
+constexpr int64_t kTableBytesLimit = int64_t(UINT32_MAX);
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -129,7 +131,8 @@ int validate_forward(const void *depth, int32_t depth_dtype, int64_t n_depth, co
     const bool e4m3_small = !tiles16 && feat_dtype == BEVPOOL_FP8_E4M3 && row_bytes <= 512;
     if (row_bytes % (e4m3_small ? 8 : 16) != 0 || row_bytes > 1024) return BEVPOOL_ERR_UNSUPPORTED;
 
-    if (n_cells * C > kInt32Limit || n_feat_rows * C > kInt32Limit || n_depth > kInt32Limit)
+    if (n_cells * C > kInt32Limit || n_feat_rows * C > kInt32Limit || n_depth > kInt32Limit ||
+        n_feat_rows * row_bytes > kTableBytesLimit)
         return BEVPOOL_ERR_OVERFLOW;
     if (!aligned(out, out_dtype == BEVPOOL_F32 ? 16 : 8) || (feat && !aligned(feat, 16)) ||
         (depth && !aligned(depth, uintptr_t(elem_bytes(depth_dtype)))))
@@ -231,7 +234,8 @@ int bevpool_segment_reduce(const void *weights, int32_t weight_dtype, const void
     const int64_t row_bytes = int64_t(C) * fe;
     const bool e4m3_small = table_dtype == BEVPOOL_FP8_E4M3 && row_bytes <= 512;
     if (row_bytes % (e4m3_small ? 8 : 16) != 0 || row_bytes > 1024) return BEVPOOL_ERR_UNSUPPORTED;
-    if (int64_t(n_segments) * C > kInt32Limit || n_rows * C > kInt32Limit)
+    if (int64_t(n_segments) * C > kInt32Limit || n_rows * C > kInt32Limit ||
+        n_rows * row_bytes > kTableBytesLimit)
         return BEVPOOL_ERR_OVERFLOW;
     if (!aligned(out, 16) || !aligned(table, 16) ||
         (weights && !aligned(weights, uintptr_t(elem_bytes(weight_dtype)))))

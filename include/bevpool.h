@@ -140,6 +140,9 @@ int bevpool_build_map(const int32_t *point_cell, int32_t n_img, int32_t D, int32
  *       geometry (n_points, n_intervals entries).  The kernel trusts the map:
  *       indices outside depth / feat / out are undefined behaviour.
  *   out [n_cells, C] fp32 (device, 16-byte aligned), overwritten.
+ * Sizes: n_cells*C and n_feat_rows*C below 2^31 elements, n_depth below 2^31,
+ *   and the feature table below 4 GiB (n_feat_rows*C*element bytes < 2^32;
+ *   this binds only for F32 features); else BEVPOOL_ERR_OVERFLOW.
  * Asynchronous: enqueues on `stream` and returns; never synchronises or
  * allocates, so it may be captured into a HIP graph.
  * Errors: INVALID_ARG, UNSUPPORTED, OVERFLOW, HIP (launch failure).
@@ -202,6 +205,7 @@ int bevpool_forward_ex(const void *depth, int32_t depth_dtype, int64_t n_depth,
  *       non-decreasing, offsets[n_segments] <= n_points.  The kernel trusts
  *       them (values outside the arrays are undefined behaviour).
  *   out [n_segments, C] fp32 (device, 16-byte aligned), overwritten.
+ * Sizes: n_segments*C and n_rows*C below 2^31, table below 4 GiB.
  * Asynchronous, no allocation.  n_segments == 0 is a no-op.  Errors:
  * INVALID_ARG, UNSUPPORTED, OVERFLOW, HIP.
  */

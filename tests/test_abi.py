@@ -83,6 +83,7 @@ def _fwd(lib, **kw):
     (dict(fdt=dws.FP8_E4M3, C=2048), -2),
     (dict(n_cells=1 << 26, C=64), -3),          # n_cells * C >= 2^31
     (dict(rows=1 << 26, C=64), -3),
+    (dict(ddt=dws.F32, fdt=dws.F32, rows=(1 << 24) + 1, C=64), -3),   # fp32 table of 4 GiB + 256 B
     (dict(out=FAKE + 4), -1),                   # misaligned output
     (dict(feat=FAKE + 8), -1),                  # misaligned features
 ])
@@ -159,6 +160,7 @@ def test_baseline_rejects(lib):
     (dict(tdt=dws.F16, wdt=dws.F32), -2),
     (dict(C=12), -2),
     (dict(n_seg=1 << 26, C=64), -3),
+    (dict(wdt=dws.F32, tdt=dws.F32, rows=1 << 24, C=64), -3),          # fp32 table of 4 GiB
     (dict(out=FAKE + 4), -1),
 ])
 def test_segment_reduce_rejects(lib, kw, code):

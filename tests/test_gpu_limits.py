@@ -1,0 +1,125 @@
+"""GPU parity at the size limits of the C ABI.
+
+* Feature tables just under the 4 GiB byte-offset limit (and under 2^31
+  elements), with the gathered rows at the top of the table, so the kernel's
+  32-bit unsigned row offsets run up to their largest values.
+* An output of n_cells*C just under 2^31 elements (8.6 GB of fp32), with an
+  occupied cell every 64 cells plus the first and the last cell, so every
+  element is written (checked against a NaN fill) and the empty ones are 0.
+
+The oracle works on the same points with the occupied cells renumbered
+densely and only the gathered rows kept: renaming cells and rows changes no
+sum, and it keeps the host-side arrays small.
+"""
+import numpy as np
+import pytest
+import torch
+
+import depth_weighted_scatter_amd as dws
+import oracle
+import workloads as W
+from gpu_util import check_forward, dev, say, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+INT32_MAX = 2 ** 31 - 1
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    oracle.build(force=False)
+    dws._load()
+
+
+def _map_from_cells(cells: np.ndarray, ranks_depth: np.ndarray, ranks_feat: np.ndarray) -> dict:
+    """Five-array map for points already ordered by cell (non-decreasing)."""
+    N = cells.size
+    starts = np.flatnonzero(np.r_[True, cells[1:] != cells[:-1]]).astype(np.int32)
+    lengths = np.diff(np.r_[starts, N]).astype(np.int32)
+    return {"ranks_depth": ranks_depth.astype(np.int32), "ranks_feat": ranks_feat.astype(np.int32),
+            "ranks_bev": cells.astype(np.int32), "interval_starts": starts,
+            "interval_lengths": lengths, "n_points": N, "n_intervals": starts.size}
+
+
+def _gpu_map(m: dict) -> dws.BevMap:
+    return dws.BevMap(*(to_gpu(m[k]) for k in ("ranks_depth", "ranks_feat", "ranks_bev",
+                                                 "interval_starts", "interval_lengths")),
+                      n_points=m["n_points"], n_intervals=m["n_intervals"])
+
+
+LARGE_TABLES = [("f16", 80), ("f32", 64), ("e4m3", 512)]
+
+
+@pytest.mark.parametrize("feat_dtype,C", LARGE_TABLES, ids=[f"{a}-C{b}" for a, b in LARGE_TABLES])
+def test_forward_largest_feature_table(feat_dtype, C):
+    eb = {"f32": 4, "f16": 2, "e4m3": 1}[feat_dtype]
+    n_rows = min(INT32_MAX // C, (2 ** 32 - 1) // (C * eb))
+    say(f"[largest table {feat_dtype} C={C}] rows={n_rows} bytes={n_rows * C * eb}")
+    rng = np.random.default_rng(41)
+    # rows used: the top 200 of the table and 100 elsewhere
+    used = np.unique(np.r_[np.arange(n_rows - 200, n_rows), rng.integers(0, n_rows, 100)])
+    vals = rng.standard_normal((used.size, C))
+    scale = 1.0
+    if feat_dtype == "f32":
+        vals, tdt, ddt = vals.astype(np.float32), torch.float32, np.float32
+    elif feat_dtype == "f16":
+        vals, tdt, ddt = vals.astype(np.float16), torch.float16, np.float16
+    else:
+        vals, scale = W.quantize_e4m3(vals.astype(np.float16))
+        tdt, ddt = torch.uint8, np.float16
+    # points: 40 cells, lengths 1..300 (some past the one-wave limit)
+    n_cells = 40
+    lengths = np.r_[rng.integers(1, 40, 35), [97, 150, 300, 1, 200]]
+    cells = np.repeat(np.sort(rng.choice(n_cells + 20, n_cells, replace=False)), lengths)
+    n_cells += 20
+    N = cells.size
+    pick = rng.integers(0, used.size, N)
+    n_depth = 5000
+    depth = rng.random(n_depth).astype(ddt)
+    ranks_depth = rng.integers(0, n_depth, N)
+    m_gpu = _map_from_cells(cells, ranks_depth, used[pick])
+    m_ref = _map_from_cells(cells, ranks_depth, pick)          # rows renumbered densely
+
+    feat = torch.zeros((n_rows, C), dtype=tdt, device=dev())
+    feat[torch.from_numpy(used).to(dev())] = torch.from_numpy(vals).to(dev())
+    out = torch.full((n_cells, C), float("nan"), dtype=torch.float32, device=dev())
+    dws.bevpool_forward(to_gpu(depth), feat, _gpu_map(m_gpu), n_cells, feat_scale=scale, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    del feat
+    torch.cuda.empty_cache()
+    ref, ref_abs = oracle.forward(depth, vals, feat_dtype, scale, C, m_ref, n_cells, with_abs=True)
+    check_forward(got, ref, ref_abs, feat_dtype, m_ref["ranks_bev"], f"table {feat_dtype}")
+
+
+def test_forward_largest_output():
+    C = 8
+    n_cells = INT32_MAX // C                                    # 268,435,455 cells, 8.6 GB fp32
+    rng = np.random.default_rng(43)
+    occ = np.r_[0, np.arange(64, n_cells - 1, 64), n_cells - 1].astype(np.int64)
+    lengths = rng.integers(1, 4, occ.size)
+    cells = np.repeat(occ, lengths)
+    N = cells.size
+    n_rows, n_depth = 10000, 4096
+    feat = rng.standard_normal((n_rows, C)).astype(np.float16)
+    depth = rng.random(n_depth).astype(np.float16)
+    ranks_depth = rng.integers(0, n_depth, N)
+    ranks_feat = rng.integers(0, n_rows, N)
+    say(f"[largest output] n_cells={n_cells} occupied={occ.size} points={N}")
+    m_gpu = _map_from_cells(cells, ranks_depth, ranks_feat)
+    dense = np.repeat(np.arange(occ.size), lengths)               # occupied cells renumbered
+    m_ref = _map_from_cells(dense, ranks_depth, ranks_feat)
+
+    out = torch.full((n_cells, C), float("nan"), dtype=torch.float32, device=dev())
+    dws.bevpool_forward(to_gpu(depth), to_gpu(feat), _gpu_map(m_gpu), n_cells, out=out)
+    torch.cuda.synchronize()
+    occ_t = torch.from_numpy(occ).to(dev())
+    got = out.index_select(0, occ_t).cpu().numpy()
+    out.index_fill_(0, occ_t, 0.0)
+    assert not bool((out != 0).any()), "an empty cell is not 0 (or an element was not written)"
+    del out
+    torch.cuda.empty_cache()
+    ref, ref_abs = oracle.forward(depth, feat, "f16", 1.0, C, m_ref, occ.size, with_abs=True)
+    check_forward(got, ref, ref_abs, "f16", np.arange(occ.size), "largest output")

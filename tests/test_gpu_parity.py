@@ -178,6 +178,27 @@ def test_forward_length_one_intervals_bit_exact(feat_dtype, C):
     assert np.array_equal(got, out_ref.astype(np.float32))
 
 
+@pytest.mark.parametrize("C", [80, 128])
+def test_forward_length_two_intervals_bit_exact(C):
+    """Two points per cell, fp16 inputs: each product d * f is exact in fp32
+    and the two land in different slots of the owner, so the output is one
+    fp32 addition of exact values, i.e. the exact sum rounded once to fp32 --
+    what the oracle's fp64 sum (exact here) rounds to."""
+    rng = np.random.default_rng(13)
+    n_img, D, H, Wd = 1, 4, 8, 16
+    P = n_img * D * H * Wd
+    n_cells = P // 2 + 5
+    cells = np.repeat(rng.permutation(n_cells)[:P // 2], 2).astype(np.int32)
+    pc = rng.permutation(cells).astype(np.int32)
+    depth, feat, scale = _make_inputs(rng, n_img, D, H, Wd, C, "f16")
+    say(f"[length-2 f16 C={C}]")
+    ref = oracle.build_map(pc, n_img, D, H, Wd, n_cells)
+    assert (ref["interval_lengths"] == 2).all()
+    out_ref = oracle.forward(depth, feat, "f16", scale, C, ref, n_cells)
+    got = gpu_forward(depth, feat, scale, map_from_numpy(ref), n_cells, C)
+    assert np.array_equal(got, out_ref.astype(np.float32))
+
+
 def test_forward_e4m3_every_code():
     """All 254 finite e4m3 codes through the kernel's native fp8 decode."""
     C = 16
