@@ -149,6 +149,7 @@ int validate_forward(const void *depth, int32_t depth_dtype, int64_t n_depth, co
     p.ranks_bev = ranks_bev;
     p.interval_starts = interval_starts;
     p.interval_lengths = interval_lengths;
+    p.n_points = n_points;
     p.n_intervals = n_intervals;
     p.out = out;
     p.out_dtype = out_dtype;
@@ -249,6 +250,7 @@ int bevpool_segment_reduce(const void *weights, int32_t weight_dtype, const void
     p.chunks = int32_t(row_bytes / 16);
     p.ranks_feat = indices;
     p.interval_starts = offsets;
+    p.n_points = n_points;
     p.n_intervals = n_segments;
     p.out = out;
     p.out_dtype = bevpool::kF32;

@@ -38,7 +38,7 @@ struct FwdParams {
     int32_t C;
     int32_t chunks;              // 16-byte chunks per feature row (= G lanes per point)
     const int32_t *ranks_depth, *ranks_feat, *ranks_bev, *interval_starts, *interval_lengths;
-    int32_t n_intervals;
+    int32_t n_points, n_intervals;
     int32_t n_long_blocks;       // blocks in the long-interval role (set by run_forward)
     void *out;                   // [n_cells, C] of out_dtype, 16-byte aligned
     int32_t out_dtype;           // kF32, kF16 or kBF16

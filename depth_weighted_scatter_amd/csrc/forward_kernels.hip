@@ -26,8 +26,11 @@
 //     section "Map the algorithm to hardware").
 //   * Cells without points: intervals come in increasing cell order, so the
 //     owner of interval i also zeroes the cells between the previous
-//     interval's cell and its own, and the last owner zeroes the tail; every
-//     output element is stored exactly once and no memset is needed.
+//     interval's cell and its own.  Long empty runs are shared out so no
+//     single wave writes them: the head and tail of the grid are sliced over
+//     the first and last 64 owners, and aligned chunks of 256 cells that lie
+//     inside a gap are zeroed by chunk checks run on the long-interval blocks.
+//     Every output element is stored exactly once and no memset is needed.
 //
 // The kernel is latency-bound (a 209K-point frame moves ~10 MB through HBM),
 // so the launch is shaped for memory-level parallelism:
@@ -147,6 +150,95 @@ __device__ inline void zero_cells(void *out, int out_dtype, int C, int cell_lo, 
         for (int q = q0 + lane; q < q1; q += lanes)
             __builtin_nontemporal_store(z, static_cast<u32x2 *>(out) + q);
     }
+}
+
+// The empty cells before the first interval's cell (the head) and after the
+// last one's (the tail) can be long runs -- a grid wider than the sensing
+// range, or a region no camera sees.  They are cut into up to 64 slices of at
+// least kSliceCells cells: slice s of the head is zeroed by the owner of
+// interval s, slice s of the tail by the owner of interval I - 1 - s.  Both
+// ends are known from ranks_bev[0] and ranks_bev[N - 1], so no owner waits on
+// another.  The gaps between intervals are zeroed by the owner of the
+// interval that follows them.
+constexpr int kSliceCells = 64;
+
+struct Slice { int lo, hi; };
+
+// Slice s of the cells [lo, hi) shared by `owners` owners.
+__device__ inline Slice end_slice(int lo, int hi, int s, int owners)
+{
+    const int size = hi - lo;
+    const int k = max(1, min(min(kWave, owners), (size + kSliceCells - 1) / kSliceCells));
+    if (s >= k || size <= 0) return {0, 0};
+    const int len = (size + k - 1) / k;
+    return {min(hi, lo + s * len), min(hi, lo + (s + 1) * len)};
+}
+
+// This owner's slices of the head and tail.
+__device__ inline void zero_end_slices(const FwdParams &p, int od, int C, int iv, int lane,
+                                       int lanes)
+{
+    if (iv < kWave) {
+        const Slice h = end_slice(0, p.ranks_bev[0], iv, p.n_intervals);
+        zero_cells(p.out, od, C, h.lo, h.hi, lane, lanes);
+    }
+    const int s_tail = p.n_intervals - 1 - iv;
+    if (s_tail < kWave) {
+        const Slice t = end_slice(p.ranks_bev[p.n_points - 1] + 1, p.n_cells, s_tail, p.n_intervals);
+        zero_cells(p.out, od, C, t.lo, t.hi, lane, lanes);
+    }
+}
+
+// Empty cells between two intervals (an interior gap) are zeroed by the owner
+// of the interval that follows the gap, except for the aligned chunks of
+// kChunkCells cells that lie wholly inside the gap: the long-interval blocks,
+// after their own intervals, check every chunk (zero_chunk_if_empty) and
+// zero the empty ones, so a long interior gap is spread over many waves and
+// an owner zeroes at most two partial chunks.
+constexpr int kChunkCells = 256;
+
+__device__ inline void zero_interior_gap(const FwdParams &p, int od, int C, int lo, int hi,
+                                         int lane, int lanes)
+{
+    if (hi - lo >= kChunkCells) {          // may hold whole chunks: those are the workers'
+        const int kf = (lo + kChunkCells - 1) / kChunkCells, kl = hi / kChunkCells;
+        if (kf < kl) {
+            zero_cells(p.out, od, C, lo, kf * kChunkCells, lane, lanes);
+            lo = kl * kChunkCells;
+        }
+    }
+    zero_cells(p.out, od, C, lo, hi, lane, lanes);
+}
+
+// Chunk check: zeroes cells [c0, c0 + kChunkCells) if no point falls in
+// them and they lie between the first and the last occupied cell.  The first
+// point whose cell is >= c0 is found by a 64-way search over ranks_bev, which
+// is sorted by cell.
+__device__ inline void zero_chunk_if_empty(const FwdParams &p, int od, int C, int chunk, int lane)
+{
+    const int c0 = chunk * kChunkCells, c1 = min(p.n_cells, c0 + kChunkCells);
+    const int N = p.n_points;
+    const int first = p.ranks_bev[0], last = p.ranks_bev[N - 1];
+    if (c1 <= first || c0 > last) return;          // head or tail: sliced elsewhere
+    // the first t with ranks_bev[t] >= c0 lies in [lo, hi]; hv = ranks_bev[hi]
+    // (INT32_MAX while hi = N, i.e. no such point yet)
+    int lo = 0, hi = N, hv = INT32_MAX;
+    while (lo < hi) {
+        const int step = (hi - lo + kWave - 1) / kWave;
+        const int t = lo + lane * step;
+        const bool valid = t < hi;
+        const int v = valid ? p.ranks_bev[t] : INT32_MAX;   // probes past hi count as >= c0
+        const uint64_t ge = __ballot(v >= c0);
+        const int j = ge ? __builtin_ctzll(ge) : kWave;
+        // the answer is in (t_(j-1), min(t_j, hi)], with t_(-1) = lo - 1
+        const int new_lo = j == 0 ? lo : lo + (j - 1) * step + 1;
+        if (j < kWave && lo + j * step < hi) {
+            hi = lo + j * step;
+            hv = __builtin_amdgcn_readlane(v, j);
+        }
+        lo = new_lo;
+    }
+    if (hv >= c1) zero_cells(p.out, od, C, c0, c1, lane, kWave);   // no point in [c0, c1)
 }
 
 // Lane i reads the map indices of point t0 + min(i, n - 1), 1 <= n <= 64:
@@ -293,7 +385,10 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
         if (iv >= p.n_intervals) return;
         const int start = p.interval_starts[iv];
         const int len = SEG ? p.interval_starts[iv + 1] - start : p.interval_lengths[iv];
-        if (len > kShortMax) return;                       // owned by a long-interval block
+        if (len > kShortMax) {                              // owned by a long-interval block
+            if (!SEG) zero_end_slices(p, od, C, iv, lane, kWave);
+            return;
+        }
         // lane 0: the cell before this interval, other lanes: its own cell
         const int cells = SEG ? iv - 1 + min(lane, 1) : p.ranks_bev[max(start - 1 + min(lane, 1), 0)];
 #pragma unroll
@@ -304,9 +399,10 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
             if (FT == kE4M3) sum *= scale;
             store4(p.out, od, bev * C4 + q, sum);
         });
-        const int prev_bev = iv > 0 ? __builtin_amdgcn_readlane(cells, 0) : -1;
-        zero_cells(p.out, od, C, prev_bev + 1, bev, lane, kWave);
-        if (iv == p.n_intervals - 1) zero_cells(p.out, od, C, bev + 1, p.n_cells, lane, kWave);
+        if (!SEG) {
+            if (iv > 0) zero_interior_gap(p, od, C, __builtin_amdgcn_readlane(cells, 0) + 1, bev, lane, kWave);
+            zero_end_slices(p, od, C, iv, lane, kWave);
+        }
         return;
     }
 
@@ -345,11 +441,15 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
                 if (FT == kE4M3) sum *= scale;
                 store4(p.out, od, bev * C4 + q, sum);
             }
-            zero_cells(p.out, od, C, prev_bev + 1, bev, threadIdx.x, kBlock);
-            if (iv == p.n_intervals - 1)
-                zero_cells(p.out, od, C, bev + 1, p.n_cells, threadIdx.x, kBlock);
+            if (!SEG && iv > 0) zero_interior_gap(p, od, C, prev_bev + 1, bev, threadIdx.x, kBlock);
             __syncthreads();                                // part is reused
         }
+    }
+    // then each wave checks its share of the cell chunks for interior gaps
+    if (!SEG) {
+        const int n_chunks = (p.n_cells + kChunkCells - 1) / kChunkCells;
+        for (int c = blockIdx.x * kWavesPerBlock + wv; c < n_chunks; c += nl * kWavesPerBlock)
+            zero_chunk_if_empty(p, od, C, c, lane);
     }
 }
 

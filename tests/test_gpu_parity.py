@@ -249,6 +249,59 @@ def test_forward_edge_cases(case):
         assert (got == 0).all()
 
 
+GAP_CASES = ["head", "tail", "head_and_tail_one_cell", "interior_two_clusters",
+             "many_interior_gaps", "gaps_around_chunk_sizes", "sparse_random", "half_rows_empty"]
+
+
+@pytest.mark.parametrize("case", GAP_CASES)
+def test_forward_large_empty_regions(case):
+    """Maps with long runs of empty cells (grid wider than the occupied area,
+    regions no point reaches, gaps of 255..513 cells around the 256-cell
+    chunking): every empty cell must come out exactly 0 and every occupied
+    cell must match the oracle."""
+    rng = np.random.default_rng(100 + GAP_CASES.index(case))
+    n_img, D, H, Wd, C = 1, 8, 16, 40, 16
+    P = n_img * D * H * Wd
+    n_cells = 60000
+    if case == "head":
+        pc = rng.integers(n_cells - 3000, n_cells, P)
+    elif case == "tail":
+        pc = rng.integers(0, 3000, P)
+    elif case == "head_and_tail_one_cell":
+        pc = np.full(P, 31337)
+    elif case == "interior_two_clusters":
+        pc = np.where(rng.random(P) < 0.5, rng.integers(0, 500, P), rng.integers(n_cells - 500, n_cells, P))
+    elif case == "many_interior_gaps":
+        base = rng.integers(0, 40, P) * 1500
+        pc = base + rng.integers(0, 300, P)
+    elif case == "gaps_around_chunk_sizes":
+        # occupied cells separated by gaps of 255, 256, 257, 511, 512, 513, 1024 cells,
+        # some starting on a chunk boundary
+        edges, c = [], 100
+        for g in [255, 256, 257, 511, 512, 513, 1024, 1, 300, 768]:
+            edges.append(c)
+            c += g + 1
+        edges.append(1024 * 20)
+        edges.append(1024 * 20 + 257)
+        pc = rng.choice(np.array(edges), P)
+    elif case == "sparse_random":
+        pc = rng.choice(n_cells, 200, replace=False)[rng.integers(0, 200, P)]
+    else:   # half_rows_empty: a 240 x 250 grid with rows 60..179 empty
+        rows = rng.integers(0, 120, P)
+        rows = np.where(rows >= 60, rows + 120, rows)
+        pc = rows * 250 + rng.integers(0, 250, P)
+    pc = pc.astype(np.int32)
+    pc[rng.random(P) < 0.2] = -1
+    depth, feat, scale = _make_inputs(rng, n_img, D, H, Wd, C, "f16")
+    say(f"[forward large empty regions: {case}]")
+    ref = oracle.build_map(pc, n_img, D, H, Wd, n_cells)
+    m = gpu_map(pc, n_img, D, H, Wd, n_cells)
+    assert_maps_equal(map_to_numpy(m), ref, case)
+    out_ref, out_abs = oracle_reference(depth, feat, "f16", scale, C, ref, n_cells)
+    got = gpu_forward(depth, feat, scale, m, n_cells, C)
+    check_forward(got, out_ref, out_abs, "f16", ref["ranks_bev"], case)
+
+
 def test_forward_graph_replay_matches_eager():
     """Captured forward calls replayed several times, with eager work and
     synchronisations in between; every replay must equal the eager result."""
