@@ -32,7 +32,7 @@
 //     inside a gap are zeroed by chunk checks run on the long-interval blocks.
 //     Every output element is stored exactly once and no memset is needed.
 //
-// The kernel is latency-bound (a 209K-point frame moves ~10 MB through HBM),
+// The kernel is latency-bound (a 209K-point frame moves ~19 MB through HBM),
 // so the launch is shaped for memory-level parallelism:
 //   * Short intervals (<= 96 points, ~99% of them at 209K points) get one
 //     wave each, in blocks of four, with a small register budget (about 18
