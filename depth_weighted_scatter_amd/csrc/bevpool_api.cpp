@@ -151,6 +151,7 @@ int validate_forward(const void *depth, int32_t depth_dtype, int64_t n_depth, co
     p.interval_lengths = interval_lengths;
     p.n_points = n_points;
     p.n_intervals = n_intervals;
+    p.table_bytes = n_feat_rows * row_bytes;
     p.out = out;
     p.out_dtype = out_dtype;
     p.n_cells = int32_t(n_cells);
@@ -252,6 +253,7 @@ int bevpool_segment_reduce(const void *weights, int32_t weight_dtype, const void
     p.interval_starts = offsets;
     p.n_points = n_points;
     p.n_intervals = n_segments;
+    p.table_bytes = n_rows * row_bytes;
     p.out = out;
     p.out_dtype = bevpool::kF32;
     p.n_cells = n_segments;

@@ -45,8 +45,13 @@
 //     each one's points, and the partial rows are summed through LDS in wave
 //     order before the single write.  These blocks are dispatched first, so
 //     the long intervals overlap the short ones.
-//   Blocks go out in interval order (no XCD remapping): giving each XCD a
-//   contiguous range of cells piled the long intervals onto one or two XCDs.
+//   * Blocks go out to the eight XCDs round-robin.  When the feature table is
+//     much larger than one XCD's 4 MB L2 (a batch of frames), each XCD is
+//     instead given one contiguous eighth of the short intervals, so its L2
+//     holds the rows of its own cells (one frame's rows, for a batch) rather
+//     than every XCD streaming the whole table.  Below that size the plain
+//     order is kept: contiguous eighths of one frame are unequal in work
+//     (dense cells near the cameras).
 #include <hip/hip_runtime.h>
 
 #include "bevpool_internal.h"
@@ -66,6 +71,7 @@ constexpr int kBlock = kWave * kWavesPerBlock;
 constexpr int kShortMax = 96;   // longest interval a single wave owns
 constexpr int kRoundPoints = 18; // points per row-request round of a wave
 constexpr int kLongScan = 16;    // intervals scanned per long-interval block
+constexpr int64_t kContiguousTableBytes = int64_t(8) << 20;   // two XCD L2s
 
 // A lane's share of a feature row: CB bytes (16, or 8 for e4m3 rows up to
 // 512 bytes, which keeps e4m3 on the same ten-lane row geometry as fp16).
@@ -381,7 +387,11 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
 
     if (int(blockIdx.x) >= p.n_long_blocks) {
         // ---- short-interval role: one wave, one interval ----
-        const int iv = (blockIdx.x - p.n_long_blocks) * kWavesPerBlock + wv;
+        // Block j of this role runs on XCD (j + n_long_blocks) mod 8; with
+        // xcd_run > 1 XCD x takes the logical blocks [x * run, (x + 1) * run).
+        const int j = blockIdx.x - p.n_long_blocks;
+        const int lj = p.xcd_run == 1 ? j : ((j + p.n_long_blocks) % 8) * p.xcd_run + j / 8;
+        const int iv = lj * kWavesPerBlock + wv;
         if (iv >= p.n_intervals) return;
         const int start = p.interval_starts[iv];
         const int len = SEG ? p.interval_starts[iv + 1] - start : p.interval_lengths[iv];
@@ -465,7 +475,11 @@ hipError_t launch_typed(FwdParams p, hipStream_t s)
 {
     // long-interval blocks: about kLongScan intervals scanned per block
     p.n_long_blocks = min(2048, max(1, (p.n_intervals + kLongScan - 1) / kLongScan));
-    const int blocks = p.n_long_blocks + (p.n_intervals + kWavesPerBlock - 1) / kWavesPerBlock;
+    // short-role blocks: contiguous eighths per XCD for BEV tables over 8 MB
+    // (segment rows follow no cell order, so segments keep the plain order)
+    const int short_blocks = (p.n_intervals + kWavesPerBlock - 1) / kWavesPerBlock;
+    p.xcd_run = !SEG && p.table_bytes > kContiguousTableBytes ? (short_blocks + 7) / 8 : 1;
+    const int blocks = p.n_long_blocks + (p.xcd_run == 1 ? short_blocks : 8 * p.xcd_run);
     const size_t lds = size_t(kWavesPerBlock) * p.C * sizeof(float);
 #define BEVPOOL_CASE(GV)                                                             \
     case GV: bev_pool_fwd<DT, FT, CB, GV, SEG><<<blocks, kBlock, lds, s>>>(p); break;
