@@ -8,7 +8,7 @@
 //     tiles);
 //   * V2+DO ("depth-outer"): each interval is visited once and all of its
 //     channels are accumulated in that visit.
-// Neither kernel's source is on the pages; these are our own plain HIP
+// Neither kernel's source is in the article; these are our own plain HIP
 // versions of the two loop orders, with the same inputs and outputs as
 // bevpool_forward, for measuring the ladder on MI355X.  One thread owns one
 // (interval, 16-byte channel tile) pair and walks the interval's points; the

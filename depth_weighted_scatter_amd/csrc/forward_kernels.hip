@@ -9,7 +9,7 @@
 // every channel locally and writes the cell once -- no atomics, and the map
 // arrays carry explicit indices so nothing is divided at run time.
 //
-// CDNA4 mapping (our design, not the pages'):
+// CDNA4 mapping (our design, not the article's):
 //   * A feature row is split into G chunks of 16 bytes (8 bytes for e4m3 rows
 //     up to 512 bytes); lane (g, k) = g*G + k loads chunk k of point slot g,
 //     so one wave instruction gathers PPW = 64/G rows (C=80 fp16 or e4m3:
@@ -22,7 +22,7 @@
 //     OCP-fp8 v_cvt_pk_f32_fp8; accumulation is fp32 in registers.
 //   * The PPW slot accumulators of a wave are folded through LDS and the cell
 //     is written with non-temporal 16-byte stores, so the output stream does
-//     not evict feature rows from L2 (the pages' cache-streaming stores,
+//     not evict feature rows from L2 (the article's cache-streaming stores,
 //     section "Map the algorithm to hardware").
 //   * Cells without points: intervals come in increasing cell order, so the
 //     owner of interval i also zeroes the cells between the previous

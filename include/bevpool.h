@@ -9,13 +9,16 @@
  *
  *     out[ranks_bev[t], c] += depth[ranks_depth[t]] * feat[ranks_feat[t], c]
  *
- * The library has two calls.  bevpool_build_map turns a per-point cell index
- * into the five-array INT32 scatter map of that section (ranks_depth,
- * ranks_feat, ranks_bev, interval_starts, interval_lengths), once per
- * geometry.  bevpool_forward runs the interval-owned scatter-reduce of
- * section "Implement the interval-owned scatter-reduce": each interval of
- * points sharing one cell has a single owner that accumulates all channels
- * and writes the cell once; no atomics, no runtime index division.
+ * bevpool_build_map turns a per-point cell index into the five-array INT32
+ * scatter map of that section (ranks_depth, ranks_feat, ranks_bev,
+ * interval_starts, interval_lengths), once per geometry.  bevpool_forward runs
+ * the interval-owned scatter-reduce of section "Implement the interval-owned
+ * scatter-reduce": each interval of points sharing one cell has a single
+ * owner that accumulates all channels and writes the cell once; no atomics,
+ * no runtime index division.  bevpool_forward_ex adds fp16/bf16 output cells,
+ * bevpool_segment_reduce applies the same owner kernel to a weighted
+ * segmented gather-reduce (an embedding bag), and bevpool_forward_baseline
+ * runs the article's two earlier loop orders for comparison.
  *
  * Conventions (all calls):
  *   - Pointers without an h_ prefix are device pointers (HBM of the current
@@ -25,8 +28,8 @@
  *     Arguments are validated on the host before any HIP call, so a failed
  *     validation touches neither the GPU nor any output.
  *   - Work is enqueued on `stream` (NULL = the null stream).
- *   - Sizes follow the pages' INT32 map contract: point counts, cell counts
- *     times C, and feature rows times C must stay below 2^31.
+ *   - Sizes follow the article's INT32 map contract: point counts, cell
+ *     counts times C, and feature rows times C must stay below 2^31.
  */
 #ifndef BEVPOOL_H
 #define BEVPOOL_H

@@ -17,7 +17,7 @@
  *     prepared in advance; an interval is a run of points with the same
  *     ranks_bev and its cell is ranks_bev[start]; every output cell is
  *     written once.
- * The pages leave the map's construction open.  Readings used here:
+ * The article leaves the map's construction open.  Readings used here:
  *   points are the frustum points whose cell is >= 0; they are ordered by
  *   the key (cell, frustum index p), a total order, so the map is unique;
  *   intervals are the maximal runs of equal cell in that order, listed in
