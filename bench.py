@@ -63,6 +63,10 @@ def parse():
                     help="(CPU) turn rocprofv3 csv output of this benchmark into a summary under "
                          "profiles/ and update profiles/traffic.json, then exit")
     ap.add_argument("--commands", default="", help="with --summarize: the commands that made the inputs")
+    ap.add_argument("--pmc-dirs", nargs="*", default=[],
+                    help="with --summarize: further rocprofv3 --pmc output directories whose "
+                         "counters for the forward kernel are listed (L2 hit rate from "
+                         "TCC_HIT_sum / TCC_MISS_sum when present)")
     return ap.parse_args()
 
 
@@ -167,6 +171,19 @@ def summarize(args):
               f"- calibration factors: fetch {f_scale}, write {w_scale}",
               f"- forward HBM bytes per call (calibrated): {traffic}",
               f"- kernel source sha256[:16]: {bench['secondary']['kernel_sha256_16']}", ""]
+    extra = {}
+    for d in args.pmc_dirs:
+        for r in _read_csv(d, "counter_collection.csv"):
+            if "bev_pool_fwd" in r["Kernel_Name"]:
+                extra.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if extra:
+        lines += ["## Further counters (rocprofv3 --pmc, mean per dispatch of the forward kernel)", ""]
+        for k in sorted(extra):
+            lines.append(f"- {k}: {sum(extra[k]) / len(extra[k]):.4g}")
+        if "TCC_HIT_sum" in extra and "TCC_MISS_sum" in extra:
+            hit, miss = sum(extra["TCC_HIT_sum"]), sum(extra["TCC_MISS_sum"])
+            lines.append(f"- L2 (TCC) hit rate: {100 * hit / max(hit + miss, 1):.1f} %")
+        lines.append("")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     out_md = os.path.join(ROOT, "profiles", f"{name}_{workload}.md")
     with open(out_md, "w") as f:
