@@ -65,7 +65,8 @@ def test_map_bit_exact_random(seed):
 
 
 @pytest.mark.parametrize("case", ["all_dropped", "one_point", "one_cell", "single_cell_grid",
-                                  "tile_minus_1", "tile_plus_1", "last_cell_only"])
+                                  "tile_minus_1", "tile_plus_1", "last_cell_only",
+                                  "cells_near_int32_max"])
 def test_map_edge_cases(case):
     rng = np.random.default_rng(7)
     n_img, D, H, Wd, n_cells = 1, 1, 1, 5000, 64
@@ -87,6 +88,12 @@ def test_map_edge_cases(case):
         pc[pc >= 0] = 0
     elif case == "last_cell_only":
         pc[::3] = n_cells - 1
+    elif case == "cells_near_int32_max":
+        # the largest grid the map allows: every radix digit, the top one included
+        n_cells = (1 << 31) - 1
+        pc = rng.integers(n_cells - 3000, n_cells, P).astype(np.int32)
+        pc[::7] = rng.integers(0, 1 << 16, pc[::7].size)
+        pc[::11] = -1
     say(f"[map edge {case}] P={P} n_cells={n_cells}")
     ref = oracle.build_map(pc, n_img, D, H, Wd, n_cells)
     got = map_to_numpy(gpu_map(pc, n_img, D, H, Wd, n_cells))
