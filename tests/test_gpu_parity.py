@@ -341,6 +341,68 @@ def test_forward_graph_replay_matches_eager():
             assert torch.equal(o, eager), f"replay {rep} differs from eager"
 
 
+def test_forward_ex_and_segment_reduce_graph_replay():
+    """The narrow-output forward (on the batched frame, whose feature table
+    takes the XCD-contiguous block order) and the segmented reduce, captured
+    together and replayed with eager work between replays, match eager calls
+    bit for bit."""
+    wl, s, _ = _workload_case(4)
+    m = gpu_map(wl.point_cell, s.n_img, s.D, s.H, s.W, s.n_cells)
+    depth, feat = to_gpu(wl.depth), to_gpu(wl.feat)
+    b = W.make_bags(1)
+    w, t = to_gpu(b.weights), to_gpu(b.table)
+    idx, off = to_gpu(b.indices), to_gpu(b.offsets)
+    eager_f = dws.bevpool_forward_ex(depth, feat, m, s.n_cells, out_dtype=torch.float16)
+    eager_b = dws.bevpool_segment_reduce(w, t, idx, off)
+    torch.cuda.synchronize()
+    out_f, out_b = torch.empty_like(eager_f), torch.empty_like(eager_b)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dws.bevpool_forward_ex(depth, feat, m, s.n_cells, out_dtype=torch.float16, out=out_f)
+        dws.bevpool_segment_reduce(w, t, idx, off, out=out_b)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dws.bevpool_forward_ex(depth, feat, m, s.n_cells, out_dtype=torch.float16, out=out_f)
+        dws.bevpool_segment_reduce(w, t, idx, off, out=out_b)
+    for rep in range(3):
+        out_f.fill_(float("nan"))
+        out_b.fill_(float("nan"))
+        _ = (t.float() * 2).sum()                   # unrelated eager work
+        torch.cuda.synchronize()
+        say(f"  graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_f.view(torch.int16), eager_f.view(torch.int16)), f"forward_ex replay {rep}"
+        assert torch.equal(out_b.view(torch.int32), eager_b.view(torch.int32)), f"segments replay {rep}"
+
+
+def test_forward_concurrent_streams_match_serial():
+    """Calls on two streams at once (different maps and outputs) give the
+    results of serial calls: the library keeps no state between calls."""
+    wa, sa, _ = _workload_case(1)
+    wb, sb, _ = _workload_case(3)
+    ma = gpu_map(wa.point_cell, sa.n_img, sa.D, sa.H, sa.W, sa.n_cells)
+    mb = gpu_map(wb.point_cell, sb.n_img, sb.D, sb.H, sb.W, sb.n_cells)
+    da, fa, db, fb = to_gpu(wa.depth), to_gpu(wa.feat), to_gpu(wb.depth), to_gpu(wb.feat)
+    ref_a = dws.bevpool_forward(da, fa, ma, sa.n_cells)
+    ref_b = dws.bevpool_forward(db, fb, mb, sb.n_cells)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs_a = [torch.full_like(ref_a, float("nan")) for _ in range(4)]
+    outs_b = [torch.full_like(ref_b, float("nan")) for _ in range(4)]
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for oa, ob in zip(outs_a, outs_b):
+        dws.bevpool_forward(da, fa, ma, sa.n_cells, out=oa, stream=s1)
+        dws.bevpool_forward(db, fb, mb, sb.n_cells, out=ob, stream=s2)
+    torch.cuda.synchronize()
+    for oa, ob in zip(outs_a, outs_b):
+        assert torch.equal(oa, ref_a) and torch.equal(ob, ref_b)
+
+
 def _cells_with_lengths(rng, lengths, n_cells_extra=7, gaps=True):
     """point_cell for a 1 x 1 x 1 x P frustum whose kept points form one
     interval per requested length, in shuffled frustum order."""
