@@ -208,7 +208,9 @@ def cpu_baseline(wl, b_alg, seconds):
     import oracle
     oracle.build(force=False)
     s = wl.spec
+    tm = time.perf_counter()
     ref_map = oracle.build_map(wl.point_cell, s.n_img, s.D, s.H, s.W, s.n_cells)
+    map_ms = (time.perf_counter() - tm) * 1e3
     reps, t0 = 0, time.perf_counter()
     while True:
         oracle.forward(wl.depth, wl.feat, s.feat_dtype, wl.feat_scale, s.C, ref_map, s.n_cells)
@@ -221,7 +223,19 @@ def cpu_baseline(wl, b_alg, seconds):
             "sample": f"{reps} full passes of the oracle's fp64 scatter-reduce over the "
                       f"{s.name} workload (N={ref_map['n_points']}), {el:.1f} s, single thread",
             "us_per_call": round(per * 1e6, 1),
-            "cpu": platform.processor() or platform.machine()}
+            "map_build_ms": round(map_ms, 1),
+            "cpu": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def bench_bags(args):
