@@ -41,6 +41,8 @@ struct FwdParams {
     int32_t n_points, n_intervals;
     int32_t n_long_blocks;       // blocks in the long-interval role (set by run_forward)
     int32_t xcd_run;             // short-role blocks per XCD run (set by run_forward; 1 = plain order)
+    int32_t first_short;         // first short-role block of a launch (set by run_forward)
+    int32_t short_base;          // logical short-role block of that block (set by run_forward)
     int64_t table_bytes;         // feature-table bytes (n_feat_rows * row bytes)
     void *out;                   // [n_cells, C] of out_dtype, 16-byte aligned
     int32_t out_dtype;           // kF32, kF16 or kBF16

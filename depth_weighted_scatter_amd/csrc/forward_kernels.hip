@@ -52,6 +52,15 @@
 //     than every XCD streaming the whole table.  Below that size the plain
 //     order is kept: contiguous eighths of one frame are unequal in work
 //     (dense cells near the cameras).
+//   * Segment reductions (embedding bags) can hold segments of thousands of
+//     points.  With rows of 16 or more chunks, a segment over kPartMin points
+//     is split by channels into four parts, worked by four blocks at once:
+//     the owning long-interval block and one block from each of three
+//     channel-part groups dispatched after the long-interval blocks.  Each
+//     part is written once, so no cross-block combine is needed.
+//   * One launch holds at most kMaxShortBlocks short-role blocks (its grid of
+//     work-items must stay below 2^32); more intervals take further launches
+//     of short-role blocks only.
 #include <hip/hip_runtime.h>
 
 #include "bevpool_internal.h"
@@ -71,6 +80,12 @@ constexpr int kBlock = kWave * kWavesPerBlock;
 constexpr int kShortMax = 96;   // longest interval a single wave owns
 constexpr int kRoundPoints = 18; // points per row-request round of a wave
 constexpr int kLongScan = 16;    // intervals scanned per long-interval block
+constexpr int kPartScan = 256;   // segments scanned per channel-part block
+constexpr int kPartMin = 384;    // segments longer than this are split by channels
+// short-role blocks per launch at most (a multiple of 8); more intervals take
+// further launches of short-role blocks only, which keeps every grid's
+// work-item count below 2^32
+constexpr int kMaxShortBlocks = 1 << 22;
 constexpr int64_t kContiguousTableBytes = int64_t(8) << 20;   // two XCD L2s
 
 // A lane's share of a feature row: CB bytes (16, or 8 for e4m3 rows up to
@@ -263,10 +278,30 @@ __device__ inline void load_indices(const FwdParams &p, int t0, int n, int lane,
     didx = SEG ? t : p.ranks_depth[t];
 }
 
+// Channel parts a long segment of a segment reduction is split into: 4 for
+// rows of 16 or more chunks (a multiple of 4), else 1 (whole rows; also when
+// the chunk count is known only at run time).  Rows of 16 chunks take four
+// points per load instruction whole and sixteen per part; rows of 8 chunks
+// measured slower split in two or four.  BEV pooling keeps whole rows: with
+// its few, moderately long intervals the extra blocks cost more than they save.
+template <bool SEG>
+__host__ __device__ constexpr int channel_parts(int g)
+{
+    return SEG && g >= 16 && g % 4 == 0 ? 4 : 1;
+}
+
+// Blocks in each channel-part group after the first.
+__host__ __device__ inline int part_blocks(int n_intervals)
+{
+    return max(1, (n_intervals + kPartScan - 1) / kPartScan);
+}
+
 // Lane geometry of a wave: lane (g, k) = g*G + k holds chunk k of slot g.
 struct Slots {
     int G, PPW, g, k, lane;
-    bool ok;   // g < PPW (the last 64 mod G lanes idle)
+    bool ok;     // g < PPW (the last 64 mod G lanes idle)
+    int row_G;   // chunks per feature row (G unless one channel part is worked)
+    int coff;    // first chunk of the part worked (0 for whole rows)
 };
 
 // Accumulates points [t0, t0 + n) (n >= 1) into this lane's acc, in batches
@@ -287,7 +322,7 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
     for (int base = 0; base < n; base += kWave) {
         const int nb = min(kWave, n - base);
         const bool more = base + kWave < n;                // wave-uniform
-        const int my_chunk = row0 * s.G;
+        const int my_chunk = row0 * s.row_G + s.coff;
         DRaw draw = DRaw(0);
         int row1 = 0, didx1 = 0;
         for (int s0 = 0; s0 < nb; s0 += SUB * s.PPW) {
@@ -381,16 +416,21 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
     s.k = lane - s.g * s.G;
     s.lane = lane;
     s.ok = s.g < s.PPW;
+    s.row_G = s.G;
+    s.coff = 0;
     const float scale = FT == kE4M3 ? p.feat_scale : 1.f;
     const int od = p.out_dtype;
     float acc[E];
 
-    if (int(blockIdx.x) >= p.n_long_blocks) {
+    constexpr int KP = channel_parts<SEG>(G_CT);
+    const int first_short = p.first_short;
+    if (int(blockIdx.x) >= first_short) {
         // ---- short-interval role: one wave, one interval ----
-        // Block j of this role runs on XCD (j + n_long_blocks) mod 8; with
-        // xcd_run > 1 XCD x takes the logical blocks [x * run, (x + 1) * run).
-        const int j = blockIdx.x - p.n_long_blocks;
-        const int lj = p.xcd_run == 1 ? j : ((j + p.n_long_blocks) % 8) * p.xcd_run + j / 8;
+        // Logical block j of this role runs on XCD (j + first_short) mod 8
+        // (short_base is a multiple of 8); with xcd_run > 1 XCD x takes the
+        // logical blocks [x * run, (x + 1) * run).
+        const int j = int(blockIdx.x) - first_short + p.short_base;
+        const int lj = p.xcd_run == 1 ? j : ((j + first_short) % 8) * p.xcd_run + j / 8;
         const int iv = lj * kWavesPerBlock + wv;
         if (iv >= p.n_intervals) return;
         const int start = p.interval_starts[iv];
@@ -416,40 +456,64 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
         return;
     }
 
-    // ---- long-interval role: block b owns the long intervals b, b+n, ... ----
-    const int nl = p.n_long_blocks;
-    for (int base = blockIdx.x; base < p.n_intervals; base += nl * kWave) {
+    // ---- long-interval role ----
+    // Group 0 (the first n_long_blocks blocks): block b owns the long
+    // intervals b, b + n_long_blocks, ...  With KP > 1 a segment over kPartMin
+    // points is split by channels into KP parts: group 0 works part 0, and
+    // group j (n_part blocks each, after group 0) works part j, its block b
+    // taking the segments b, b + n_part, ...  Every part is written once.
+    const int n_part = KP > 1 ? part_blocks(p.n_intervals) : 0;
+    const int grp = KP == 1 || int(blockIdx.x) < p.n_long_blocks
+                        ? 0 : 1 + (int(blockIdx.x) - p.n_long_blocks) / n_part;
+    const int nl = grp == 0 ? p.n_long_blocks : n_part;
+    const int b0 = grp == 0 ? int(blockIdx.x) : (int(blockIdx.x) - p.n_long_blocks) % n_part;
+    const int min_len = grp == 0 ? kShortMax : kPartMin;
+    Slots sp = s;                                           // lane geometry of one part
+    if (KP > 1) {
+        sp.G = s.G / KP;
+        sp.PPW = kWave / sp.G;
+        sp.g = lane / sp.G;
+        sp.k = lane - sp.g * sp.G;
+        sp.ok = sp.g < sp.PPW;
+        sp.coff = grp * sp.G;
+    }
+    const int Cp = C / KP, Cp4 = Cp / 4;
+    for (int base = b0; base < p.n_intervals; base += nl * kWave) {
         const int cand = base + lane * nl;
         int cand_len = 0;
         if (cand < p.n_intervals)
             cand_len = SEG ? p.interval_starts[cand + 1] - p.interval_starts[cand]
                            : p.interval_lengths[cand];
-        uint64_t todo = __ballot(cand_len > kShortMax);    // same in every wave of the block
+        uint64_t todo = __ballot(cand_len > min_len);      // same in every wave of the block
         while (todo) {
             const int j = __builtin_ctzll(todo);
             todo &= todo - 1;
             const int iv = base + j * nl;
             const int len = __builtin_amdgcn_readlane(cand_len, j);
+            const bool split = KP > 1 && len > kPartMin;
+            const Slots &ss = split ? sp : s;
+            const int Cw = split ? Cp : C, Cw4 = split ? Cp4 : C4;
+            const int c4off = split ? grp * Cp4 : 0;
             const int start = p.interval_starts[iv];
             // the four waves take consecutive quarters of the points
             const int quarter = (len + kWavesPerBlock - 1) / kWavesPerBlock;
             const int lo = min(len, wv * quarter), hi = min(len, lo + quarter);
 #pragma unroll
             for (int e = 0; e < E; ++e) acc[e] = 0.f;
-            if (lo < hi) accumulate_points<DT, FT, CB, SUB, SEG>(p, start + lo, hi - lo, s, acc);
-            fold_slots<E>(red[wv], acc, s, C, [&](int q, f32x4 sum) {
-                *reinterpret_cast<f32x4 *>(part + wv * C + 4 * q) = sum;
+            if (lo < hi) accumulate_points<DT, FT, CB, SUB, SEG>(p, start + lo, hi - lo, ss, acc);
+            fold_slots<E>(red[wv], acc, ss, Cw, [&](int q, f32x4 sum) {
+                *reinterpret_cast<f32x4 *>(part + wv * Cw + 4 * q) = sum;
             });
             __syncthreads();
             const int bev = SEG ? iv : p.ranks_bev[start];
             const int prev_bev = SEG ? iv - 1 : (iv > 0 ? p.ranks_bev[start - 1] : -1);
-            for (int q = threadIdx.x; q < C4; q += kBlock) {
+            for (int q = threadIdx.x; q < Cw4; q += kBlock) {
                 f32x4 sum = *reinterpret_cast<const f32x4 *>(part + 4 * q);
 #pragma unroll
                 for (int w = 1; w < kWavesPerBlock; ++w)
-                    sum += *reinterpret_cast<const f32x4 *>(part + w * C + 4 * q);
+                    sum += *reinterpret_cast<const f32x4 *>(part + w * Cw + 4 * q);
                 if (FT == kE4M3) sum *= scale;
-                store4(p.out, od, bev * C4 + q, sum);
+                store4(p.out, od, bev * C4 + c4off + q, sum);
             }
             if (!SEG && iv > 0) zero_interior_gap(p, od, C, prev_bev + 1, bev, threadIdx.x, kBlock);
             __syncthreads();                                // part is reused
@@ -470,6 +534,23 @@ __global__ __launch_bounds__(kBlock) void zero_fill(void *out, int out_dtype, in
         store4(out, out_dtype, i, z);
 }
 
+// The launches of one call: the first holds the long-interval blocks, the
+// channel-part groups (segment reductions with rows split into parts) and up
+// to kMaxShortBlocks short-role blocks; any further ones hold short-role
+// blocks only.
+template <int DT, int FT, int CB, int G, bool SEG>
+void launch_g(FwdParams p, int n_short, size_t lds, hipStream_t s)
+{
+    constexpr int kp = channel_parts<SEG>(G);
+    const int role_blocks = p.n_long_blocks + (kp > 1 ? (kp - 1) * part_blocks(p.n_intervals) : 0);
+    for (int base = 0; base < n_short; base += kMaxShortBlocks) {
+        p.first_short = base == 0 ? role_blocks : 0;
+        p.short_base = base;
+        const int blocks = p.first_short + min(kMaxShortBlocks, n_short - base);
+        bev_pool_fwd<DT, FT, CB, G, SEG><<<blocks, kBlock, lds, s>>>(p);
+    }
+}
+
 template <int DT, int FT, int CB, bool SEG>
 hipError_t launch_typed(FwdParams p, hipStream_t s)
 {
@@ -479,14 +560,14 @@ hipError_t launch_typed(FwdParams p, hipStream_t s)
     // (segment rows follow no cell order, so segments keep the plain order)
     const int short_blocks = (p.n_intervals + kWavesPerBlock - 1) / kWavesPerBlock;
     p.xcd_run = !SEG && p.table_bytes > kContiguousTableBytes ? (short_blocks + 7) / 8 : 1;
-    const int blocks = p.n_long_blocks + (p.xcd_run == 1 ? short_blocks : 8 * p.xcd_run);
+    const int n_short = p.xcd_run == 1 ? short_blocks : 8 * p.xcd_run;
     const size_t lds = size_t(kWavesPerBlock) * p.C * sizeof(float);
-#define BEVPOOL_CASE(GV)                                                             \
-    case GV: bev_pool_fwd<DT, FT, CB, GV, SEG><<<blocks, kBlock, lds, s>>>(p); break;
+#define BEVPOOL_CASE(GV) \
+    case GV: launch_g<DT, FT, CB, GV, SEG>(p, n_short, lds, s); break;
     switch (p.chunks) {
         BEVPOOL_CASE(1) BEVPOOL_CASE(2) BEVPOOL_CASE(4) BEVPOOL_CASE(5) BEVPOOL_CASE(8)
         BEVPOOL_CASE(10) BEVPOOL_CASE(16) BEVPOOL_CASE(20) BEVPOOL_CASE(32) BEVPOOL_CASE(64)
-    default: bev_pool_fwd<DT, FT, CB, 0, SEG><<<blocks, kBlock, lds, s>>>(p); break;
+    default: launch_g<DT, FT, CB, 0, SEG>(p, n_short, lds, s); break;
     }
 #undef BEVPOOL_CASE
     return hipGetLastError();

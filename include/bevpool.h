@@ -147,7 +147,8 @@ int bevpool_build_map(const int32_t *point_cell, int32_t n_img, int32_t D, int32
  *   and the feature table below 4 GiB (n_feat_rows*C*element bytes < 2^32;
  *   this binds only for F32 features); else BEVPOOL_ERR_OVERFLOW.
  * Asynchronous: enqueues on `stream` and returns; never synchronises or
- * allocates, so it may be captured into a HIP graph.
+ * allocates, so it may be captured into a HIP graph.  One kernel launch, or
+ * several in stream order for more than 2^24 intervals.
  * Errors: INVALID_ARG, UNSUPPORTED, OVERFLOW, HIP (launch failure).
  */
 int bevpool_forward(const void *depth, int32_t depth_dtype, int64_t n_depth,
@@ -198,7 +199,10 @@ int bevpool_forward_ex(const void *depth, int32_t depth_dtype, int64_t n_depth,
  *               weights[t] * table[indices[t], c] (* table_scale for e4m3)
  *
  * with one owner per segment, fp32 accumulation and one write per output
- * element; empty segments are written as 0.
+ * element; empty segments are written as 0.  For wide rows (fp32: C a
+ * multiple of 16 and at least 64; fp16 and e4m3: C a multiple of 32 and at
+ * least 128, and of 64 past 512 for e4m3) a segment of over 384 points gets
+ * four owners, one per quarter of the channels, each writing its quarter once.
  *
  *   weights [n_points] (device; NULL = all ones), weight_dtype as the depth
  *       dtype of bevpool_forward.

@@ -123,3 +123,61 @@ def test_forward_largest_output():
     torch.cuda.empty_cache()
     ref, ref_abs = oracle.forward(depth, feat, "f16", 1.0, C, m_ref, occ.size, with_abs=True)
     check_forward(got, ref, ref_abs, "f16", np.arange(occ.size), "largest output")
+
+
+# More than 2^24 intervals: the short-role blocks (one interval per wave)
+# exceed one launch's cap of 2^22 blocks and continue in a second launch.
+# A small table keeps the plain block order; one over 8 MB takes the
+# XCD-contiguous order, whose logical blocks then span both launches.
+MANY = 17_000_000
+
+
+@pytest.mark.parametrize("table_rows", [1000, 600_000], ids=["plain-order", "xcd-order"])
+def test_forward_more_intervals_than_one_launch(table_rows):
+    C = 8
+    rng = np.random.default_rng(47)
+    n_cells = MANY + 3_000_000
+    occ = np.sort(rng.permutation(n_cells)[:MANY])
+    lengths = rng.integers(1, 3, MANY)
+    lengths[rng.integers(0, MANY, 20)] = 500                      # a few long intervals
+    cells = np.repeat(occ, lengths)
+    N = cells.size
+    n_depth = 4096
+    feat = rng.standard_normal((table_rows, C)).astype(np.float16)
+    depth = rng.random(n_depth).astype(np.float16)
+    say(f"[many intervals] intervals={MANY} points={N} table rows={table_rows}")
+    m = _map_from_cells(cells, rng.integers(0, n_depth, N), rng.integers(0, table_rows, N))
+    out = torch.full((n_cells, C), float("nan"), dtype=torch.float32, device=dev())
+    dws.bevpool_forward(to_gpu(depth), to_gpu(feat), _gpu_map(m), n_cells, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    del out
+    torch.cuda.empty_cache()
+    ref, ref_abs = oracle.forward(depth, feat, "f16", 1.0, C, m, n_cells, with_abs=True)
+    check_forward(got, ref, ref_abs, "f16", m["ranks_bev"], f"many intervals rows={table_rows}")
+
+
+def test_segment_reduce_more_segments_than_one_launch():
+    C = 8                                                         # two channel parts
+    rng = np.random.default_rng(53)
+    n_seg = MANY
+    lens = (rng.random(n_seg) < 0.1).astype(np.int64)
+    lens[rng.integers(0, n_seg, 10)] = 2000                       # split by channels
+    lens[-1] = 3
+    offsets = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N = int(offsets[-1])
+    table = rng.standard_normal((5000, C)).astype(np.float32)
+    idx = rng.integers(0, 5000, N).astype(np.int32)
+    weights = rng.random(N).astype(np.float32)
+    say(f"[many segments] segments={n_seg} points={N}")
+    out = torch.full((n_seg, C), float("nan"), dtype=torch.float32, device=dev())
+    dws.bevpool_segment_reduce(to_gpu(weights), to_gpu(table), to_gpu(idx), to_gpu(offsets),
+                               out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    del out
+    torch.cuda.empty_cache()
+    ref, ref_abs = oracle.segment_reduce(weights, table, "f32", 1.0, idx, offsets, with_abs=True)
+    assert np.isfinite(got).all(), "an element was not written"
+    assert (np.abs(got - ref) <= 1e-3 * ref_abs).all()
+    assert (got[lens == 0] == 0).all()
