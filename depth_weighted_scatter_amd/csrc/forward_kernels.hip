@@ -527,11 +527,20 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
     }
 }
 
-__global__ __launch_bounds__(kBlock) void zero_fill(void *out, int out_dtype, int n4)
+// Zero output for a map with no intervals: a pure write stream, so plain
+// stores (they measured faster than non-temporal ones for bulk writes), four
+// per thread, one thread per four groups of four elements.
+constexpr int kFillPer = 4;
+
+template <class T>
+__global__ __launch_bounds__(kBlock) void zero_fill(T *out, int n4)
 {
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    for (int i = blockIdx.x * kBlock + threadIdx.x; i < n4; i += gridDim.x * kBlock)
-        store4(out, out_dtype, i, z);
+    const int i0 = blockIdx.x * (kBlock * kFillPer) + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < kFillPer; ++u) {
+        const int i = i0 + u * kBlock;
+        if (i < n4) out[i] = T{};
+    }
 }
 
 // The launches of one call: the first holds the long-interval blocks, the
@@ -602,9 +611,10 @@ hipError_t dispatch(const FwdParams &p, hipStream_t s)
 hipError_t run_forward(const FwdParams &p, hipStream_t s)
 {
     if (p.n_intervals == 0) {
-        const int n4 = p.n_cells * (p.C / 4);
-        const int blocks = min((n4 + kBlock - 1) / kBlock, 4096);
-        zero_fill<<<blocks, kBlock, 0, s>>>(p.out, p.out_dtype, n4);
+        const int n4 = p.n_cells * (p.C / 4);                 // groups of four elements
+        const int blocks = (n4 + kBlock * kFillPer - 1) / (kBlock * kFillPer);
+        if (p.out_dtype == kF32) zero_fill<<<blocks, kBlock, 0, s>>>(static_cast<f32x4 *>(p.out), n4);
+        else zero_fill<<<blocks, kBlock, 0, s>>>(static_cast<u32x2 *>(p.out), n4);
         return hipGetLastError();
     }
     return dispatch<false>(p, s);

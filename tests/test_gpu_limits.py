@@ -158,26 +158,34 @@ def test_forward_more_intervals_than_one_launch(table_rows):
 
 
 def test_segment_reduce_more_segments_than_one_launch():
-    C = 8                                                         # two channel parts
+    # fp32 rows of 64 channels are 16 chunks, so segments over 384 points are
+    # split four ways by channels (the part groups sit in the first launch)
+    C = 64
     rng = np.random.default_rng(53)
     n_seg = MANY
     lens = (rng.random(n_seg) < 0.1).astype(np.int64)
-    lens[rng.integers(0, n_seg, 10)] = 2000                       # split by channels
-    lens[-1] = 3
+    lens[rng.integers(0, n_seg, 10)] = 2000
+    lens[-1] = 3                                                  # in the second launch
     offsets = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     N = int(offsets[-1])
     table = rng.standard_normal((5000, C)).astype(np.float32)
     idx = rng.integers(0, 5000, N).astype(np.int32)
     weights = rng.random(N).astype(np.float32)
-    say(f"[many segments] segments={n_seg} points={N}")
+    say(f"[many segments] segments={n_seg} points={N} C={C}")
     out = torch.full((n_seg, C), float("nan"), dtype=torch.float32, device=dev())
     dws.bevpool_segment_reduce(to_gpu(weights), to_gpu(table), to_gpu(idx), to_gpu(offsets),
                                out=out)
     torch.cuda.synchronize()
-    got = out.cpu().numpy().astype(np.float64)
+    # the oracle sees only the non-empty segments, renumbered densely (the
+    # sums do not depend on the numbering); empty ones must be exactly zero
+    full = np.flatnonzero(lens > 0)
+    full_t = torch.from_numpy(full).to(dev())
+    got = out.index_select(0, full_t).cpu().numpy().astype(np.float64)
+    out.index_fill_(0, full_t, 0.0)
+    assert not bool((out != 0).any()), "an empty segment is not 0 (or an element was not written)"
     del out
     torch.cuda.empty_cache()
-    ref, ref_abs = oracle.segment_reduce(weights, table, "f32", 1.0, idx, offsets, with_abs=True)
+    dense = np.concatenate([[0], np.cumsum(lens[full])]).astype(np.int32)
+    ref, ref_abs = oracle.segment_reduce(weights, table, "f32", 1.0, idx, dense, with_abs=True)
     assert np.isfinite(got).all(), "an element was not written"
     assert (np.abs(got - ref) <= 1e-3 * ref_abs).all()
-    assert (got[lens == 0] == 0).all()
