@@ -435,6 +435,10 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
         if (iv >= p.n_intervals) return;
         const int start = p.interval_starts[iv];
         const int len = SEG ? p.interval_starts[iv + 1] - start : p.interval_lengths[iv];
+        // Both header words are wave-uniform (scalar loads); without this the
+        // compiler sinks the start load below the length test, so a wave
+        // would wait for two scalar round trips instead of one.
+        asm volatile("" ::"s"(start), "s"(len));
         if (len > kShortMax) {                              // owned by a long-interval block
             if (!SEG) zero_end_slices(p, od, C, iv, lane, kWave);
             return;
