@@ -238,6 +238,19 @@ def _cpu_model() -> str:
     return platform.processor() or platform.machine()
 
 
+def copy_calibration(mib, dev):
+    """A plain streaming copy of known size (read mib MiB, write mib MiB) for
+    calibrating the FETCH_SIZE / WRITE_SIZE counters of the same run."""
+    import torch
+    if not mib:
+        return
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+
+
 def bench_bags(args):
     """Weighted embedding bags through bevpool_segment_reduce (the same owner
     kernel); algorithmic bytes N*(C*e_table + e_weight + 4) + 4*(bags + 1) +
@@ -264,26 +277,38 @@ def bench_bags(args):
     for _ in range(args.warmup):
         dws.bevpool_segment_reduce(w, table, idx, off, b.table_scale, out)
     K = args.steps
-    chunk = max(1, min(args.graph_chunk, K))
-    while K % chunk:
-        chunk -= 1
-    cap = torch.cuda.Stream()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=cap):
-        a = dws.segment_reduce_args(w, table, idx, off, out, b.table_scale, cap)
-        for _ in range(chunk):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if args.eager:
+        chunk = None
+        a = dws.segment_reduce_args(w, table, idx, off, out, b.table_scale, stream)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(K):
             if lib.bevpool_segment_reduce(*a) != 0:
                 raise RuntimeError("bevpool_segment_reduce failed")
-    graph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(K // chunk):
+        e1.record(stream)
+        torch.cuda.synchronize()
+    else:
+        chunk = max(1, min(args.graph_chunk, K))
+        while K % chunk:
+            chunk -= 1
+        cap = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            a = dws.segment_reduce_args(w, table, idx, off, out, b.table_scale, cap)
+            for _ in range(chunk):
+                if lib.bevpool_segment_reduce(*a) != 0:
+                    raise RuntimeError("bevpool_segment_reduce failed")
         graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(K // chunk):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / K
     gbs = b_alg / (ms * 1e-3) / 1e9
+    copy_calibration(args.copy_calib_mib, dev)
     print(json.dumps({
         "metric": "bevpool_segment_reduce µs/call + effective GB/s (% HBM peak), weighted embedding bags",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -291,11 +316,15 @@ def bench_bags(args):
         "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (geometric bag lengths, skewed rows, N(0,1) table)",
         "config": {"workload": s.name, "bags": s.n_bags, "points": N, "table_rows": s.n_rows,
-                   "C": s.C, "table_dtype": s.table_dtype, "weighted": w is not None},
+                   "C": s.C, "table_dtype": s.table_dtype, "weighted": w is not None,
+                   "timing": "eager" if chunk is None else f"hip graph replay, {chunk} calls per graph"},
         "us_per_call": round(ms * 1e3, 3), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
-        "bytes": {"algorithmic": b_alg}}), flush=True)
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for(s.name)},
+        "bytes": {"algorithmic": b_alg},
+        "secondary": {"copy_calib_mib": args.copy_calib_mib, "kernel_sha256_16": kernel_hash()}}),
+        flush=True)
 
 
 def main():
@@ -441,14 +470,7 @@ def main():
     cold = [one_call_us(flush) for _ in range(30)]
     del flush
 
-    if args.copy_calib_mib:
-        # a plain streaming copy of known size (read n bytes, write n bytes) for
-        # calibrating the FETCH_SIZE / WRITE_SIZE counters
-        src = torch.empty(args.copy_calib_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(10):
-            torch.bitwise_not(src, out=dst)
-        torch.cuda.synchronize()
+    copy_calibration(args.copy_calib_mib, dev)
 
     workload_key = s.name if not narrow else f"{s.name}_out_{args.out_dtype}"
     traffic = traffic_for(workload_key)
