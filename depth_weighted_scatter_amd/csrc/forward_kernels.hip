@@ -94,6 +94,7 @@ template <int CB> struct ChunkVec;
 template <> struct ChunkVec<16> { using type = u32x4; };
 template <> struct ChunkVec<8> { using type = u32x2; };
 constexpr int elem_bytes(int ft) { return ft == kF32 ? 4 : ft == kF16 ? 2 : 1; }
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
 
 // Depth values are gathered in their storage type and widened at first use.
 template <int DT> struct DepthT;
@@ -403,6 +404,14 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
     constexpr int SUB_RAW = G_CT > 0 ? (kRoundPoints + PPW_CT - 1) / PPW_CT : 4;
     constexpr int SUB = G_CT >= 16 ? (SUB_RAW > 4 ? 4 : SUB_RAW)
                                    : SUB_RAW > 8 ? 8 : (SUB_RAW > 5 && E == 16 ? 5 : SUB_RAW);
+    // A channel part of a long segment (segment reductions, rows split by
+    // channels) mostly misses L2 (tables larger than it), so its waves request
+    // about 64 rows per round (at most 8 instructions) instead of
+    // kRoundPoints.  Whole rows keep SUB: registers are allocated per kernel,
+    // and more rows in flight there cost the short role its occupancy.
+    constexpr int KP = channel_parts<SEG>(G_CT);
+    constexpr int PPW_PART = G_CT > 0 ? kWave / (G_CT / KP) : 1;
+    constexpr int SUB_LP = !SEG || G_CT <= 0 ? SUB : cmin(8, (kWave + PPW_PART - 1) / PPW_PART);
     __shared__ __attribute__((aligned(16))) float red[kWavesPerBlock][kWave * E];
     extern __shared__ __attribute__((aligned(16))) float part[];   // [kWavesPerBlock][C]
 
@@ -422,7 +431,6 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
     const int od = p.out_dtype;
     float acc[E];
 
-    constexpr int KP = channel_parts<SEG>(G_CT);
     const int first_short = p.first_short;
     if (int(blockIdx.x) >= first_short) {
         // ---- short-interval role: one wave, one interval ----
@@ -504,7 +512,15 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
             const int lo = min(len, wv * quarter), hi = min(len, lo + quarter);
 #pragma unroll
             for (int e = 0; e < E; ++e) acc[e] = 0.f;
-            if (lo < hi) accumulate_points<DT, FT, CB, SUB, SEG>(p, start + lo, hi - lo, ss, acc);
+            if (lo < hi) {
+                if constexpr (SUB_LP == SUB) {
+                    accumulate_points<DT, FT, CB, SUB, SEG>(p, start + lo, hi - lo, ss, acc);
+                } else if (split) {
+                    accumulate_points<DT, FT, CB, SUB_LP, SEG>(p, start + lo, hi - lo, sp, acc);
+                } else {
+                    accumulate_points<DT, FT, CB, SUB, SEG>(p, start + lo, hi - lo, s, acc);
+                }
+            }
             fold_slots<E>(red[wv], acc, ss, Cw, [&](int q, f32x4 sum) {
                 *reinterpret_cast<f32x4 *>(part + wv * Cw + 4 * q) = sum;
             });
