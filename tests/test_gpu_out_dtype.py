@@ -72,8 +72,8 @@ def _workload_reference(k):
     return wl, ref, out_ref, out_abs
 
 
-@pytest.mark.parametrize("k", [0, 1, 2, 4])
 @pytest.mark.parametrize("out_dtype", OUT_DTYPES, ids=["f16", "bf16"])
+@pytest.mark.parametrize("k", [0, 1, 2, 4, 9])
 def test_forward_ex_narrow_output_on_workloads(out_dtype, k):
     wl, ref, out_ref, out_abs = _workload_reference(k)
     s = wl.spec

@@ -35,7 +35,7 @@ def _workload_case(k):
 
 
 # ------------------------------------------------------------------ maps
-@pytest.mark.parametrize("k", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("k", [0, 1, 2, 3, 4, 9])
 def test_map_bit_exact_on_workloads(k):
     wl, s, ref = _workload_case(k)
     m = gpu_map(wl.point_cell, s.n_img, s.D, s.H, s.W, s.n_cells)
@@ -116,7 +116,7 @@ def test_map_rejects_bad_cell_and_small_capacity():
 
 
 # --------------------------------------------------------------- forward
-@pytest.mark.parametrize("k", [0, 1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("k", [0, 1, 2, 3, 4, 5, 6, 7, 8, 9])
 def test_forward_on_workloads(k):
     wl, s, ref = _workload_case(k)
     m = gpu_map(wl.point_cell, s.n_img, s.D, s.H, s.W, s.n_cells)

@@ -99,6 +99,10 @@ SPECS = {
                     209_000, "f16", "e4m3"),
     8: WorkloadSpec("bevdet_c256_fp8", 1, 6, 59, 16, 44, 256, 128, 0.8, 1.0, 59.0,
                     209_000, "f16", "e4m3"),
+    # sixteen frames of the batched geometry: a 537 MB fp32 output, past the
+    # 256 MB Infinity Cache, so the output stream runs from HBM
+    9: WorkloadSpec("batched16_c128_fp16", 16, 6, 59, 32, 88, 128, 256, 0.4, 1.0, 59.0,
+                    6_400_000, "f16", "f16"),
 }
 
 
