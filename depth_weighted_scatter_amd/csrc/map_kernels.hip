@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kBlock) void scan_tiles(const int *in, int *out, co
 hipError_t exclusive_scan(const int *in, int *out, const int *n_dev, int n_max, int *partials,
                           int *total_out, hipStream_t s)
 {
-    const int nb = (n_max + kTile - 1) / kTile;
+    const int nb = int((int64_t(n_max) + kTile - 1) / kTile);   // n_max may be 2^31 - 1
     if (nb == 0) return hipSuccess;
     scan_reduce_tiles<<<nb, kBlock, 0, s>>>(in, n_dev, n_max, partials);
     scan_partials<<<1, 1024, 0, s>>>(partials, nb, total_out);
@@ -341,7 +341,10 @@ hipError_t run_build_map(const MapParams &mp, int32_t h_counts[3], hipStream_t s
         src ^= 1;
     }
 
-    const int grid = (P + kBlock - 1) / kBlock;
+    // Grid sizes are rounded up in 64 bits (P may be 2^31 - 1).  In the kernels
+    // no index passes 2^31 - 1: tiles of kTile and blocks of kBlock elements
+    // divide 2^31, so the last tile or block ends at or below it.
+    const int grid = int((int64_t(P) + kBlock - 1) / kBlock);
     emit_ranks<<<grid, kBlock, 0, s>>>(kin, vin, counters, mp.capacity, mp.DHW, mp.HW,
                                        mp.ranks_depth, mp.ranks_feat, mp.ranks_bev, w.flags);
     e = exclusive_scan(w.flags, w.flags, counters, P, w.partials, counters + 1, s);

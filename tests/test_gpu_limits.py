@@ -18,7 +18,7 @@ import torch
 import depth_weighted_scatter_amd as dws
 import oracle
 import workloads as W
-from gpu_util import check_forward, dev, say, to_gpu
+from gpu_util import check_forward, dev, map_to_numpy, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -189,3 +189,31 @@ def test_segment_reduce_more_segments_than_one_launch():
     ref, ref_abs = oracle.segment_reduce(weights, table, "f32", 1.0, idx, dense, with_abs=True)
     assert np.isfinite(got).all(), "an element was not written"
     assert (np.abs(got - ref) <= 1e-3 * ref_abs).all()
+
+
+def test_build_map_largest_frustum():
+    # n_img*D*H*W = 2^31 - 1, the largest frustum the map builder takes, with
+    # kept points spread over it and packed into its last few thousand indices
+    # (the last tile and the last emission block).
+    P = INT32_MAX
+    n_cells = 5000
+    rng = np.random.default_rng(59)
+    kept = np.unique(np.r_[rng.integers(0, P, 1_200_000), np.arange(P - 3000, P), [0, 1, 2]])
+    cells = rng.integers(0, n_cells, kept.size).astype(np.int32)
+    say(f"[largest frustum] P={P} kept={kept.size}")
+    pc = torch.full((P,), -1, dtype=torch.int32, device=dev())
+    pc[torch.from_numpy(kept).to(dev())] = torch.from_numpy(cells).to(dev())
+    m = dws.bevpool_build_map(pc, 1, 1, 1, P, n_cells, capacity=kept.size)
+    del pc
+    torch.cuda.empty_cache()
+    # The oracle sees only the kept points, renumbered 0..K-1 in order.  The
+    # renumbering keeps their order, so the sorted order is the same; with one
+    # image, one depth bin and one row the feature row of p is p itself.
+    ref = oracle.build_map(cells, 1, 1, 1, kept.size, n_cells)
+    got = map_to_numpy(m)
+    assert got["n_points"] == ref["n_points"] == kept.size
+    assert got["n_intervals"] == ref["n_intervals"]
+    assert np.array_equal(got["ranks_depth"], kept[ref["ranks_depth"]])
+    assert np.array_equal(got["ranks_feat"], kept[ref["ranks_feat"]])
+    for k in ("ranks_bev", "interval_starts", "interval_lengths"):
+        assert np.array_equal(got[k], ref[k]), k
