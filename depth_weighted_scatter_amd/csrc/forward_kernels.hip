@@ -32,8 +32,9 @@
 //     inside a gap are zeroed by chunk checks run on the long-interval blocks.
 //     Every output element is stored exactly once and no memset is needed.
 //
-// The kernel is latency-bound (a 209K-point frame moves ~19 MB through HBM),
-// so the launch is shaped for memory-level parallelism:
+// The kernel is not bandwidth-bound on a single frame (a 209K-point frame
+// moves ~19 MB through HBM in ~6 us): its time is waves waiting on short chains
+// of dependent loads, so the launch is shaped for memory-level parallelism:
 //   * Short intervals (<= 96 points, ~99% of them at 209K points) get one
 //     wave each, in blocks of four, with a small register budget (about 18
 //     points' rows in flight per request round) so seven or eight waves fit
@@ -57,7 +58,11 @@
 //     is split by channels into four parts, worked by four blocks at once:
 //     the owning long-interval block and one block from each of three
 //     channel-part groups dispatched after the long-interval blocks.  Each
-//     part is written once, so no cross-block combine is needed.
+//     part is written once, so no cross-block combine is needed.  Waves of a
+//     long segment of unsplit rows stage a few more row loads per round
+//     straight into LDS (global_load_lds), so more rows are in flight without
+//     registers, which are allocated per kernel and would cost the short role
+//     its occupancy.
 //   * One launch holds at most kMaxShortBlocks short-role blocks (its grid of
 //     work-items must stay below 2^32); more intervals take further launches
 //     of short-role blocks only.
@@ -95,6 +100,15 @@ template <> struct ChunkVec<16> { using type = u32x4; };
 template <> struct ChunkVec<8> { using type = u32x2; };
 constexpr int elem_bytes(int ft) { return ft == kF32 ? 4 : ft == kF16 ? 2 : 1; }
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
+// Row loads a wave stages in LDS per round when it works a long segment of
+// unsplit rows: enough for about kStagePoints points per round with the SUB
+// register-held loads, at most kMaxStaged (3 KB of LDS per wave).
+constexpr int kStagePoints = 48;
+constexpr int kMaxStaged = 3;
+constexpr int staged_loads(int ppw, int sub)
+{
+    return cmin(kMaxStaged, (kStagePoints + ppw - 1) / ppw - sub > 0 ? (kStagePoints + ppw - 1) / ppw - sub : 0);
+}
 
 // Depth values are gathered in their storage type and widened at first use.
 template <int DT> struct DepthT;
@@ -310,9 +324,11 @@ struct Slots {
 // only the row indices), then the batch's depth values, then the indices of
 // the next batch; accumulation waits for all of it.  Rows of a batch are
 // requested SUB sub-iterations (SUB*PPW points) at a time.
-template <int DT, int FT, int CB, int SUB, bool SEG>
+typedef __attribute__((address_space(3))) char lds_char;
+
+template <int DT, int FT, int CB, int SUB, bool SEG, int LST = 0>
 __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, const Slots &s,
-                                         float *acc)
+                                         float *acc, lds_char *stage = nullptr)
 {
     using V = typename ChunkVec<CB>::type;
     using DRaw = typename DepthT<DT>::type;
@@ -326,19 +342,27 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
         const int my_chunk = row0 * s.row_G + s.coff;
         DRaw draw = DRaw(0);
         int row1 = 0, didx1 = 0;
-        for (int s0 = 0; s0 < nb; s0 += SUB * s.PPW) {
+        for (int s0 = 0; s0 < nb; s0 += (SUB + LST) * s.PPW) {
             // Every lane loads an in-bounds row (lanes past the batch repeat
             // its last point, k < G); slots without a point are skipped by
             // exec mask when accumulating.  Only wave-uniform guards branch.
-            int rows[SUB];
+            int rows[SUB + LST];
 #pragma unroll
-            for (int u = 0; u < SUB; ++u)
+            for (int u = 0; u < SUB + LST; ++u)
                 rows[u] = __shfl(my_chunk, (s0 + u * s.PPW + s.g) & (kWave - 1));
             V v[SUB];
 #pragma unroll
             for (int u = 0; u < SUB; ++u)
                 if (s0 + u * s.PPW < nb)
                     v[u] = *reinterpret_cast<const V *>(feat + uint32_t(rows[u] + s.k) * uint32_t(CB));
+            // further rows of the round go straight to LDS: lane i's 16 bytes
+            // of staged instruction j at stage + 1024 j + 16 i
+#pragma unroll
+            for (int u = SUB; u < SUB + LST; ++u)
+                if (s0 + u * s.PPW < nb)
+                    __builtin_amdgcn_global_load_lds(
+                        (const void *)(feat + uint32_t(rows[u] + s.k) * uint32_t(CB)),
+                        (__attribute__((address_space(3))) void *)(stage + (u - SUB) * 1024), 16, 0, 0);
             if (s0 == 0) {
                 draw = (SEG && !depth) ? DRaw(1) : depth[didx0];   // segments may be unweighted
                 if (more)
@@ -346,13 +370,21 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
                                       row1, didx1);
             }
             const float my_d = static_cast<float>(draw);
-            float ds[SUB];
+            float ds[SUB + LST];
 #pragma unroll
-            for (int u = 0; u < SUB; ++u) ds[u] = __shfl(my_d, (s0 + u * s.PPW + s.g) & (kWave - 1));
+            for (int u = 0; u < SUB + LST; ++u) ds[u] = __shfl(my_d, (s0 + u * s.PPW + s.g) & (kWave - 1));
 #pragma unroll
             for (int u = 0; u < SUB; ++u) {
                 if (s0 + u * s.PPW < nb) {
                     if (s.ok && s0 + u * s.PPW + s.g < nb) Accum<FT, CB>::run(acc, ds[u], v[u]);
+                }
+            }
+#pragma unroll
+            for (int u = SUB; u < SUB + LST; ++u) {
+                if (s0 + u * s.PPW < nb) {
+                    typedef __attribute__((address_space(3))) const V lds_v;
+                    const V x = *reinterpret_cast<lds_v *>(stage + (u - SUB) * 1024 + s.lane * 16);
+                    if (s.ok && s0 + u * s.PPW + s.g < nb) Accum<FT, CB>::run(acc, ds[u], x);
                 }
             }
         }
@@ -412,7 +444,13 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
     constexpr int KP = channel_parts<SEG>(G_CT);
     constexpr int PPW_PART = G_CT > 0 ? kWave / (G_CT / KP) : 1;
     constexpr int SUB_LP = !SEG || G_CT <= 0 ? SUB : cmin(8, (kWave + PPW_PART - 1) / PPW_PART);
-    __shared__ __attribute__((aligned(16))) float red[kWavesPerBlock][kWave * E];
+    // Long segments of unsplit rows: their waves also stage LST row loads per
+    // round in LDS (the wave's fold buffer, free while it accumulates), which
+    // adds rows in flight without the registers that would cost the short
+    // role its occupancy.
+    constexpr int LST = SEG && KP == 1 && CB == 16 && G_CT > 0 ? staged_loads(PPW_CT, SUB) : 0;
+    constexpr int RED = kWave * E > LST * 256 ? kWave * E : LST * 256;   // floats per wave
+    __shared__ __attribute__((aligned(16))) float red[kWavesPerBlock][RED];
     extern __shared__ __attribute__((aligned(16))) float part[];   // [kWavesPerBlock][C]
 
     const int C = p.C, C4 = C / 4;
@@ -513,7 +551,10 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
 #pragma unroll
             for (int e = 0; e < E; ++e) acc[e] = 0.f;
             if (lo < hi) {
-                if constexpr (SUB_LP == SUB) {
+                if constexpr (LST > 0) {
+                    accumulate_points<DT, FT, CB, SUB, SEG, LST>(p, start + lo, hi - lo, s, acc,
+                                                                 (lds_char *)(__attribute__((address_space(3))) void *)red[wv]);
+                } else if constexpr (SUB_LP == SUB) {
                     accumulate_points<DT, FT, CB, SUB, SEG>(p, start + lo, hi - lo, ss, acc);
                 } else if (split) {
                     accumulate_points<DT, FT, CB, SUB_LP, SEG>(p, start + lo, hi - lo, sp, acc);
