@@ -534,3 +534,37 @@ def test_segment_reduce_edge_cases(case):
     got = _gpu_segment_reduce(w, table, 1.0, idx, off)
     nonempty = np.nonzero(np.diff(off) > 0)[0]
     check_forward(got, ref, ref_abs, dtype, nonempty, case)
+
+
+# Long segments of unsplit rows (2, 4, 5, 8 or 10 chunks) take the long role
+# with staged row loads; rows of 16 or more chunks are split by channels.
+# Lengths sit around the long-role threshold (96), the 64-point index batches
+# a wave's quarter falls into, and the channel-split threshold (384).
+LONG_SEGMENT_ROWS = [("f32", 8), ("f32", 16), ("f32", 20), ("f32", 32), ("f32", 40),
+                     ("f16", 16), ("f16", 32), ("f16", 40), ("f16", 64), ("f16", 80),
+                     ("f16", 128), ("f16", 256), ("e4m3", 80), ("e4m3", 128)]
+
+
+@pytest.mark.parametrize("table_dtype,C", LONG_SEGMENT_ROWS,
+                         ids=[f"{a}-C{b}" for a, b in LONG_SEGMENT_ROWS])
+def test_segment_reduce_long_segment_lengths(table_dtype, C):
+    rng = np.random.default_rng(61 + C)
+    lens = np.array([97, 100, 127, 128, 129, 255, 256, 257, 259, 383, 384, 385, 386, 600,
+                     1001, 4099, 3, 0, 96, 1])
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    rows = 3000
+    idx = rng.integers(0, rows, size=int(off[-1])).astype(np.int32)
+    table = rng.standard_normal((rows, C))
+    scale = 1.0
+    if table_dtype == "f32":
+        table, w = table.astype(np.float32), rng.random(idx.size).astype(np.float32)
+    elif table_dtype == "f16":
+        table, w = table.astype(np.float16), rng.random(idx.size).astype(np.float16)
+    else:
+        table, scale = W.quantize_e4m3(table.astype(np.float16))
+        w = rng.random(idx.size).astype(np.float16)
+    say(f"[long segments {table_dtype} C={C}] N={int(off[-1])}")
+    ref, ref_abs = oracle.segment_reduce(w, table, table_dtype, scale, idx, off, with_abs=True)
+    got = _gpu_segment_reduce(w, table, scale, idx, off)
+    check_forward(got, ref, ref_abs, table_dtype, np.nonzero(lens > 0)[0],
+                  f"long segments {table_dtype} C={C}")
