@@ -319,14 +319,16 @@ struct Slots {
     int coff;    // first chunk of the part worked (0 for whole rows)
 };
 
-// Accumulates points [t0, t0 + n) (n >= 1) into this lane's acc, in batches
-// of 64 points.  For each batch the feature rows go out first (they need
-// only the row indices), then the batch's depth values, then the indices of
-// the next batch; accumulation waits for all of it.  Rows of a batch are
-// requested SUB sub-iterations (SUB*PPW points) at a time.
 typedef __attribute__((address_space(3))) char lds_char;
 
-template <int DT, int FT, int CB, int SUB, bool SEG, int LST = 0>
+// Accumulates points [t0, t0 + n) (n >= 1) into this lane's acc, in batches
+// of BATCH (at most 64) points.  For each batch the feature rows go out first
+// (they need only the row indices), then the batch's depth values, then the
+// indices of the next batch; accumulation waits for all of it.  Rows of a
+// batch are requested SUB register-held loads plus LST loads staged in LDS at
+// `stage` ((SUB + LST) * PPW points) per round.
+
+template <int DT, int FT, int CB, int SUB, bool SEG, int LST = 0, int BATCH = kWave>
 __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, const Slots &s,
                                          float *acc, lds_char *stage = nullptr)
 {
@@ -335,10 +337,10 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
     const DRaw *depth = static_cast<const DRaw *>(p.depth);
     const char *feat = static_cast<const char *>(p.feat);
     int row0, didx0;
-    load_indices<SEG>(p, t0, min(kWave, n), s.lane, row0, didx0);
-    for (int base = 0; base < n; base += kWave) {
-        const int nb = min(kWave, n - base);
-        const bool more = base + kWave < n;                // wave-uniform
+    load_indices<SEG>(p, t0, min(BATCH, n), s.lane, row0, didx0);
+    for (int base = 0; base < n; base += BATCH) {
+        const int nb = min(BATCH, n - base);
+        const bool more = base + BATCH < n;                // wave-uniform
         const int my_chunk = row0 * s.row_G + s.coff;
         DRaw draw = DRaw(0);
         int row1 = 0, didx1 = 0;
@@ -366,7 +368,7 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
             if (s0 == 0) {
                 draw = (SEG && !depth) ? DRaw(1) : depth[didx0];   // segments may be unweighted
                 if (more)
-                    load_indices<SEG>(p, t0 + base + kWave, min(kWave, n - base - kWave), s.lane,
+                    load_indices<SEG>(p, t0 + base + BATCH, min(BATCH, n - base - BATCH), s.lane,
                                       row1, didx1);
             }
             const float my_d = static_cast<float>(draw);
@@ -450,6 +452,11 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
     // role its occupancy.
     constexpr int LST = SEG && KP == 1 && CB == 16 && G_CT > 0 ? staged_loads(PPW_CT, SUB) : 0;
     constexpr int RED = kWave * E > LST * 256 ? kWave * E : LST * 256;   // floats per wave
+    // Their index batches match the round when it covers 48 or more points, so
+    // no round trip is spent on a batch's short remainder (36-point rounds
+    // measured faster with 64-point batches).
+    constexpr int LROUND = (SUB + LST) * PPW_CT;
+    constexpr int LBATCH = LST > 0 && LROUND >= 48 && LROUND <= kWave ? LROUND : kWave;
     __shared__ __attribute__((aligned(16))) float red[kWavesPerBlock][RED];
     extern __shared__ __attribute__((aligned(16))) float part[];   // [kWavesPerBlock][C]
 
@@ -552,7 +559,7 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
             for (int e = 0; e < E; ++e) acc[e] = 0.f;
             if (lo < hi) {
                 if constexpr (LST > 0) {
-                    accumulate_points<DT, FT, CB, SUB, SEG, LST>(p, start + lo, hi - lo, s, acc,
+                    accumulate_points<DT, FT, CB, SUB, SEG, LST, LBATCH>(p, start + lo, hi - lo, s, acc,
                                                                  (lds_char *)(__attribute__((address_space(3))) void *)red[wv]);
                 } else if constexpr (SUB_LP == SUB) {
                     accumulate_points<DT, FT, CB, SUB, SEG>(p, start + lo, hi - lo, ss, acc);
