@@ -116,7 +116,7 @@ def test_map_rejects_bad_cell_and_small_capacity():
 
 
 # --------------------------------------------------------------- forward
-@pytest.mark.parametrize("k", [0, 1, 2, 3, 4, 5, 6, 7, 8, 9])
+@pytest.mark.parametrize("k", [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
 def test_forward_on_workloads(k):
     wl, s, ref = _workload_case(k)
     m = gpu_map(wl.point_cell, s.n_img, s.D, s.H, s.W, s.n_cells)

@@ -103,6 +103,10 @@ SPECS = {
     # 256 MB Infinity Cache, so the output stream runs from HBM
     9: WorkloadSpec("batched16_c128_fp16", 16, 6, 59, 32, 88, 128, 256, 0.4, 1.0, 59.0,
                     6_400_000, "f16", "f16"),
+    # four frames of the BEVDet-like geometry in one call: the per-call fixed
+    # cost shared by four frames
+    10: WorkloadSpec("bevdet4_c80_fp16", 4, 6, 59, 16, 44, 80, 128, 0.8, 1.0, 59.0,
+                     836_000, "f16", "f16"),
 }
 
 
