@@ -420,12 +420,14 @@ __device__ inline void fold_slots(float *r, const float *acc, const Slots &s, in
 }
 
 // CB: bytes per lane chunk.  G_CT > 0: lanes per point (chunks per row)
-// fixed at compile time; G_CT == 0: p.chunks.
+// fixed at compile time; G_CT == 0: p.chunks.  OD: the output type, fixed at
+// compile time so the stores and zero fills carry no type branches (they
+// measured 1-2 % of the call in scalar instructions).
 //
 // SEG: segment mode (bevpool_segment_reduce): interval i is segment i, with
 // start offsets[i] (interval_starts) and length offsets[i+1] - offsets[i]
 // (possibly 0), cell i, and the weight of point t read at t (or 1).
-template <int DT, int FT, int CB, int G_CT, bool SEG>
+template <int DT, int FT, int CB, int G_CT, bool SEG, int OD>
 __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
 {
     constexpr int E = CB / elem_bytes(FT);   // row elements per lane
@@ -473,7 +475,7 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
     s.row_G = s.G;
     s.coff = 0;
     const float scale = FT == kE4M3 ? p.feat_scale : 1.f;
-    const int od = p.out_dtype;
+    constexpr int od = OD;
     float acc[E];
 
     const int first_short = p.first_short;
@@ -615,7 +617,7 @@ __global__ __launch_bounds__(kBlock) void zero_fill(T *out, int n4)
 // channel-part groups (segment reductions with rows split into parts) and up
 // to kMaxShortBlocks short-role blocks; any further ones hold short-role
 // blocks only.
-template <int DT, int FT, int CB, int G, bool SEG>
+template <int DT, int FT, int CB, int G, bool SEG, int OD>
 void launch_g(FwdParams p, int n_short, size_t lds, hipStream_t s)
 {
     constexpr int kp = channel_parts<SEG>(G);
@@ -624,11 +626,11 @@ void launch_g(FwdParams p, int n_short, size_t lds, hipStream_t s)
         p.first_short = base == 0 ? role_blocks : 0;
         p.short_base = base;
         const int blocks = p.first_short + min(kMaxShortBlocks, n_short - base);
-        bev_pool_fwd<DT, FT, CB, G, SEG><<<blocks, kBlock, lds, s>>>(p);
+        bev_pool_fwd<DT, FT, CB, G, SEG, OD><<<blocks, kBlock, lds, s>>>(p);
     }
 }
 
-template <int DT, int FT, int CB, bool SEG>
+template <int DT, int FT, int CB, bool SEG, int OD>
 hipError_t launch_typed(FwdParams p, hipStream_t s)
 {
     // long-interval blocks: about kLongScan intervals scanned per block
@@ -639,15 +641,31 @@ hipError_t launch_typed(FwdParams p, hipStream_t s)
     p.xcd_run = !SEG && p.table_bytes > kContiguousTableBytes ? (short_blocks + 7) / 8 : 1;
     const int n_short = p.xcd_run == 1 ? short_blocks : 8 * p.xcd_run;
     const size_t lds = size_t(kWavesPerBlock) * p.C * sizeof(float);
+    if constexpr (FT == kE4M3 && CB == 16) {
+        // e4m3 rows take 16-byte chunks only past 512 bytes (33 chunks or more)
+        if (p.chunks == 64) launch_g<DT, FT, CB, 64, SEG, OD>(p, n_short, lds, s);
+        else launch_g<DT, FT, CB, 0, SEG, OD>(p, n_short, lds, s);
+    } else {
 #define BEVPOOL_CASE(GV) \
-    case GV: launch_g<DT, FT, CB, GV, SEG>(p, n_short, lds, s); break;
-    switch (p.chunks) {
-        BEVPOOL_CASE(1) BEVPOOL_CASE(2) BEVPOOL_CASE(4) BEVPOOL_CASE(5) BEVPOOL_CASE(8)
-        BEVPOOL_CASE(10) BEVPOOL_CASE(16) BEVPOOL_CASE(20) BEVPOOL_CASE(32) BEVPOOL_CASE(64)
-    default: launch_g<DT, FT, CB, 0, SEG>(p, n_short, lds, s); break;
-    }
+    case GV: launch_g<DT, FT, CB, GV, SEG, OD>(p, n_short, lds, s); break;
+        switch (p.chunks) {
+            BEVPOOL_CASE(1) BEVPOOL_CASE(2) BEVPOOL_CASE(4) BEVPOOL_CASE(5) BEVPOOL_CASE(8)
+            BEVPOOL_CASE(10) BEVPOOL_CASE(16) BEVPOOL_CASE(20) BEVPOOL_CASE(32) BEVPOOL_CASE(64)
+        default: launch_g<DT, FT, CB, 0, SEG, OD>(p, n_short, lds, s); break;
+        }
 #undef BEVPOOL_CASE
+    }
     return hipGetLastError();
+}
+
+// The output type as a template argument (segment reductions write fp32 only).
+template <int DT, int FT, int CB, bool SEG>
+hipError_t launch_out(const FwdParams &p, hipStream_t s)
+{
+    if (SEG || p.out_dtype == kF32) return launch_typed<DT, FT, CB, SEG, kF32>(p, s);
+    if (p.out_dtype == kF16) return launch_typed<DT, FT, CB, SEG, kF16>(p, s);
+    if (p.out_dtype == kBF16) return launch_typed<DT, FT, CB, SEG, kBF16>(p, s);
+    return hipErrorInvalidValue;
 }
 
 template <bool SEG>
@@ -657,19 +675,19 @@ hipError_t dispatch(const FwdParams &p, hipStream_t s)
     FwdParams q = p;
     if (p.depth_dtype == kF32 && p.feat_dtype == kF32) {
         q.chunks = row_bytes / 16;
-        return launch_typed<kF32, kF32, 16, SEG>(q, s);
+        return launch_out<kF32, kF32, 16, SEG>(q, s);
     }
     if (p.depth_dtype == kF16 && p.feat_dtype == kF16) {
         q.chunks = row_bytes / 16;
-        return launch_typed<kF16, kF16, 16, SEG>(q, s);
+        return launch_out<kF16, kF16, 16, SEG>(q, s);
     }
     if (p.depth_dtype == kF16 && p.feat_dtype == kE4M3) {
         if (row_bytes <= 8 * kWave) {
             q.chunks = row_bytes / 8;
-            return launch_typed<kF16, kE4M3, 8, SEG>(q, s);
+            return launch_out<kF16, kE4M3, 8, SEG>(q, s);
         }
         q.chunks = row_bytes / 16;
-        return launch_typed<kF16, kE4M3, 16, SEG>(q, s);
+        return launch_out<kF16, kE4M3, 16, SEG>(q, s);
     }
     return hipErrorInvalidValue;
 }
