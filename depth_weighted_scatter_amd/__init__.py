@@ -15,7 +15,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["BevPoolError", "BevMap", "F32", "F16", "FP8_E4M3", "library_path",
+__all__ = ["BevPoolError", "BevMap", "F32", "F16", "FP8_E4M3", "MAX_TABLE_BYTES", "library_path",
            "bevpool_status_string", "bevpool_version", "bevpool_build_map_workspace_size",
            "bevpool_build_map", "bevpool_forward", "bevpool_forward_baseline", "forward_args",
            "bevpool_forward_ex", "forward_ex_args", "BF16",
@@ -26,6 +26,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libbevpool.so")
 
 F32, F16, FP8_E4M3, BF16 = 0, 1, 2, 3
+# largest feature (or segment) table in bytes, BEVPOOL_MAX_TABLE_BYTES in bevpool.h
+MAX_TABLE_BYTES = 2 ** 32 - 4096
 ORDER_TILE_OUTER, ORDER_DEPTH_OUTER = 0, 1
 OK, ERR_CAPACITY = 0, -5
 

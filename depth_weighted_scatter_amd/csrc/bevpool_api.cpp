@@ -10,8 +10,9 @@
 namespace {
 
 constexpr int64_t kInt32Limit = int64_t(INT32_MAX);   // sizes must stay below 2^31
-// Feature rows are addressed as a table base plus a 32-bit unsigned byte offset.
-constexpr int64_t kTableBytesLimit = int64_t(UINT32_MAX);
+// Feature rows are addressed as a table base plus a 32-bit unsigned byte
+// offset, below the range the kernels keep for empty batch slots.
+constexpr int64_t kTableBytesLimit = int64_t(BEVPOOL_MAX_TABLE_BYTES);
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 

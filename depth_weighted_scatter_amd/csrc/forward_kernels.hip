@@ -13,8 +13,11 @@
 //   * A feature row is split into G chunks of 16 bytes (8 bytes for e4m3 rows
 //     up to 512 bytes); lane (g, k) = g*G + k loads chunk k of point slot g,
 //     so one wave instruction gathers PPW = 64/G rows (C=80 fp16 or e4m3:
-//     G=10, six rows per instruction).  Row loads use a scalar base and a
-//     32-bit per-lane byte offset.
+//     G=10, six rows per instruction).  Row loads are raw buffer loads with a
+//     32-bit per-lane byte offset; a slot that holds no point reads at an
+//     offset past the table, which returns zeros, with weight zero, so slots
+//     are never masked one by one (the owner waves' scalar issue is the
+//     contended resource, and per-slot exec-mask branches are scalar work).
 //   * The map indices of up to 64 points come in with one coalesced load per
 //     array; each point's depth is gathered once by the lane that read its
 //     index and handed to the lanes of its slot with ds_bpermute.
@@ -68,6 +71,7 @@
 //     of short-role blocks only.
 #include <hip/hip_runtime.h>
 
+#include "bevpool.h"
 #include "bevpool_internal.h"
 
 namespace bevpool {
@@ -278,8 +282,8 @@ __device__ inline void zero_chunk_if_empty(const FwdParams &p, int od, int C, in
 }
 
 // Lane i reads the map indices of point t0 + min(i, n - 1), 1 <= n <= 64:
-// lanes past the batch repeat its last point, so every address derived from
-// them stays in bounds and no lane needs an exec-masked branch.
+// lanes past the batch repeat its last point, so the index and depth loads
+// stay in bounds without an exec-masked branch.
 // In segment mode (SEG) the weight of point t is read directly at t.
 // These are ordinary (cached) loads: the map is reused by every call for the
 // same geometry, and streaming loads that keep it out of the caches measured
@@ -321,42 +325,88 @@ struct Slots {
 
 typedef __attribute__((address_space(3))) char lds_char;
 
-// Accumulates points [t0, t0 + n) (n >= 1) into this lane's acc, in batches
-// of BATCH (at most 64) points.  For each batch the feature rows go out first
-// (they need only the row indices), then the batch's depth values, then the
-// indices of the next batch; accumulation waits for all of it.  Rows of a
-// batch are requested SUB register-held loads plus LST loads staged in LDS at
-// `stage` ((SUB + LST) * PPW points) per round.
+// Byte offset a slot without a point reads its row at: past every table the
+// C ABI accepts (and at most 1 KB + 16 below 2^32 with a lane's chunk added),
+// so the raw buffer load there is out of range and returns zeros.
+constexpr uint32_t kEmptySlotOffset = BEVPOOL_MAX_TABLE_BYTES;
 
-template <int DT, int FT, int CB, int SUB, bool SEG, int LST = 0, int BATCH = kWave>
+// Word 3 of a raw buffer descriptor on gfx9-family chips: 32-bit data format
+// (untyped buffer loads need a valid one), no swizzle, no index stride.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+template <int CB>
+__device__ inline typename ChunkVec<CB>::type load_chunk(__amdgpu_buffer_rsrc_t rows, uint32_t off)
+{
+    if constexpr (CB == 16)
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rows, int(off), 0, 0));
+    else
+        return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rows, int(off), 0, 0));
+}
+
+// Accumulates points [t0, t0 + n) (n >= 1) into this lane's acc, in batches
+// of at most 64 points.  For each batch the loads go out in this order, and
+// accumulation waits for all of them:
+//   BEV:      depth values, feature rows, the indices of the next batch
+//             (depth first measured 0.5-1 % faster than after the rows);
+//   segments: feature rows, weights, the indices of the next batch (weights
+//             first, or fetched with the indices, measured up to 30 % slower
+//             on some segment mixes).
+// Rows of a batch are requested SUB register-held loads plus LST loads
+// staged in LDS at `stage` ((SUB + LST) * PPW points) per round.
+//
+// With PPWC (points per wave) known at compile time and rounds of at most 64
+// points (ZERO), a batch is a whole number of rounds, so a slot's point index
+// never wraps past lane 63, and the slots without a point read a zero row
+// (kEmptySlotOffset) with weight zero: every lane accumulates without a
+// branch, exactly (0 * 0 adds +0 whatever the table holds).  Otherwise
+// (PPWC == 0: G known at run time; rounds over 64 points; LDS staging) the
+// lanes past the batch repeat its last point and empty slots are skipped by
+// exec mask.  Only wave-uniform guards branch in either case.
+template <int DT, int FT, int CB, int SUB, bool SEG, int PPWC, int LST = 0>
 __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, const Slots &s,
                                          float *acc, lds_char *stage = nullptr)
 {
+    constexpr int ROUND = (SUB + LST) * (PPWC > 0 ? PPWC : kWave);
+    constexpr bool ZERO = PPWC > 0 && ROUND <= kWave && LST == 0;
+    // Staged rounds of 48 or more points take batches of one round, so no
+    // round trip is spent on a batch's short remainder (36-point rounds
+    // measured faster with 64-point batches).
+    constexpr int BATCH = ZERO ? kWave / ROUND * ROUND
+                               : LST > 0 && ROUND >= 48 && ROUND <= kWave ? ROUND : kWave;
     using V = typename ChunkVec<CB>::type;
     using DRaw = typename DepthT<DT>::type;
     const DRaw *depth = static_cast<const DRaw *>(p.depth);
     const char *feat = static_cast<const char *>(p.feat);
+    const __amdgpu_buffer_rsrc_t rows_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(feat), 0, int(kEmptySlotOffset), kRawBufferWord3);
     int row0, didx0;
     load_indices<SEG>(p, t0, min(BATCH, n), s.lane, row0, didx0);
     for (int base = 0; base < n; base += BATCH) {
         const int nb = min(BATCH, n - base);
         const bool more = base + BATCH < n;                // wave-uniform
-        const int my_chunk = row0 * s.row_G + s.coff;
-        DRaw draw = DRaw(0);
+        const bool live = s.lane < nb;                     // this lane's point is in the batch
+        // ZERO: byte offset of the lane's row (its part's first chunk);
+        // else the index of that chunk
+        const int my_row = ZERO ? int(live ? uint32_t(row0 * s.row_G + s.coff) * uint32_t(CB)
+                                           : kEmptySlotOffset)
+                                : row0 * s.row_G + s.coff;
+        DRaw draw = SEG ? DRaw(0) : depth[didx0];
         int row1 = 0, didx1 = 0;
         for (int s0 = 0; s0 < nb; s0 += (SUB + LST) * s.PPW) {
-            // Every lane loads an in-bounds row (lanes past the batch repeat
-            // its last point, k < G); slots without a point are skipped by
-            // exec mask when accumulating.  Only wave-uniform guards branch.
             int rows[SUB + LST];
 #pragma unroll
             for (int u = 0; u < SUB + LST; ++u)
-                rows[u] = __shfl(my_chunk, (s0 + u * s.PPW + s.g) & (kWave - 1));
+                rows[u] = __shfl(my_row, (s0 + u * s.PPW + s.g) & (kWave - 1));
             V v[SUB];
 #pragma unroll
-            for (int u = 0; u < SUB; ++u)
-                if (s0 + u * s.PPW < nb)
-                    v[u] = *reinterpret_cast<const V *>(feat + uint32_t(rows[u] + s.k) * uint32_t(CB));
+            for (int u = 0; u < SUB; ++u) {
+                if (s0 + u * s.PPW < nb) {
+                    if constexpr (ZERO)
+                        v[u] = load_chunk<CB>(rows_rsrc, uint32_t(rows[u]) + uint32_t(s.k * CB));
+                    else
+                        v[u] = *reinterpret_cast<const V *>(feat + uint32_t(rows[u] + s.k) * uint32_t(CB));
+                }
+            }
             // further rows of the round go straight to LDS: lane i's 16 bytes
             // of staged instruction j at stage + 1024 j + 16 i
 #pragma unroll
@@ -366,19 +416,25 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
                         (const void *)(feat + uint32_t(rows[u] + s.k) * uint32_t(CB)),
                         (__attribute__((address_space(3))) void *)(stage + (u - SUB) * 1024), 16, 0, 0);
             if (s0 == 0) {
-                draw = (SEG && !depth) ? DRaw(1) : depth[didx0];   // segments may be unweighted
+                const bool weighted = !SEG || depth;              // segments may be unweighted
+                if (SEG) draw = weighted ? depth[didx0] : DRaw(1);
                 if (more)
                     load_indices<SEG>(p, t0 + base + BATCH, min(BATCH, n - base - BATCH), s.lane,
                                       row1, didx1);
+                // Without this pin the compiler converts a segment weight
+                // right after its load, and the wait for it then holds back
+                // the next batch's indices until this batch's rows are in
+                // (13-20 % on long segments).
+                if (SEG && weighted) asm volatile("" : "+v"(draw));
             }
-            const float my_d = static_cast<float>(draw);
+            const float my_d = ZERO && !live ? 0.f : static_cast<float>(draw);
             float ds[SUB + LST];
 #pragma unroll
             for (int u = 0; u < SUB + LST; ++u) ds[u] = __shfl(my_d, (s0 + u * s.PPW + s.g) & (kWave - 1));
 #pragma unroll
             for (int u = 0; u < SUB; ++u) {
                 if (s0 + u * s.PPW < nb) {
-                    if (s.ok && s0 + u * s.PPW + s.g < nb) Accum<FT, CB>::run(acc, ds[u], v[u]);
+                    if (ZERO || (s.ok && s0 + u * s.PPW + s.g < nb)) Accum<FT, CB>::run(acc, ds[u], v[u]);
                 }
             }
 #pragma unroll
@@ -395,20 +451,21 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
     }
 }
 
-// Folds the PPW slot accumulators of a wave through its LDS scratch r and
-// hands float4 q of the C-float row sum to emit(q, sum) on lane q (mod 64).
+// Folds the PPW slot accumulators of a wave through its LDS scratch r (64*E
+// floats) and hands float4 q of the C-float row sum to emit(q, sum) on lane q
+// (mod 64).  Every lane writes its E sums unmasked: the idle lanes (g == PPW,
+// k < 64 - PPW*G) land in [PPW*C, 64*E), which the fold does not read.
 template <int E, class Emit>
 __device__ inline void fold_slots(float *r, const float *acc, const Slots &s, int C, Emit emit)
 {
-    if (s.ok) {
 #pragma unroll
-        for (int e = 0; e < E; e += 4)
-            *reinterpret_cast<f32x4 *>(r + s.g * C + s.k * E + e) =
-                f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
-    }
+    for (int e = 0; e < E; e += 4)
+        *reinterpret_cast<f32x4 *>(r + s.g * C + s.k * E + e) =
+            f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_assume(s.lane >= 0 && s.lane < kWave);   // one pass while C <= 256
     for (int q = s.lane; q < C / 4; q += kWave) {
         f32x4 sum = *reinterpret_cast<const f32x4 *>(r + 4 * q);
         for (int gg = 1; gg < s.PPW; ++gg) sum += *reinterpret_cast<const f32x4 *>(r + gg * C + 4 * q);
@@ -432,6 +489,7 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
 {
     constexpr int E = CB / elem_bytes(FT);   // row elements per lane
     constexpr int PPW_CT = G_CT > 0 ? kWave / G_CT : 1;
+    constexpr int PPW_RT = G_CT > 0 ? PPW_CT : 0;   // 0: known at run time only
     // rows in flight per lane: about kRoundPoints points per request round,
     // which keeps the common kernels near 64 VGPRs (up to eight waves per SIMD);
     // rows of 16 or more chunks (at most four points per instruction) take
@@ -448,21 +506,18 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
     constexpr int KP = channel_parts<SEG>(G_CT);
     constexpr int PPW_PART = G_CT > 0 ? kWave / (G_CT / KP) : 1;
     constexpr int SUB_LP = !SEG || G_CT <= 0 ? SUB : cmin(8, (kWave + PPW_PART - 1) / PPW_PART);
+    constexpr int PPW_PART_RT = G_CT > 0 ? PPW_PART : 0;
     // Long segments of unsplit rows: their waves also stage LST row loads per
     // round in LDS (the wave's fold buffer, free while it accumulates), which
     // adds rows in flight without the registers that would cost the short
     // role its occupancy.
     constexpr int LST = SEG && KP == 1 && CB == 16 && G_CT > 0 ? staged_loads(PPW_CT, SUB) : 0;
     constexpr int RED = kWave * E > LST * 256 ? kWave * E : LST * 256;   // floats per wave
-    // Their index batches match the round when it covers 48 or more points, so
-    // no round trip is spent on a batch's short remainder (36-point rounds
-    // measured faster with 64-point batches).
-    constexpr int LROUND = (SUB + LST) * PPW_CT;
-    constexpr int LBATCH = LST > 0 && LROUND >= 48 && LROUND <= kWave ? LROUND : kWave;
     __shared__ __attribute__((aligned(16))) float red[kWavesPerBlock][RED];
     extern __shared__ __attribute__((aligned(16))) float part[];   // [kWavesPerBlock][C]
 
-    const int C = p.C, C4 = C / 4;
+    // with a compile-time chunk count the channel count is compile-time too
+    const int C = G_CT > 0 ? G_CT * E : p.C, C4 = C / 4;
     const int lane = __lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     Slots s;
@@ -502,7 +557,7 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
         const int cells = SEG ? iv - 1 + min(lane, 1) : p.ranks_bev[max(start - 1 + min(lane, 1), 0)];
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[e] = 0.f;
-        if (!SEG || len > 0) accumulate_points<DT, FT, CB, SUB, SEG>(p, start, len, s, acc);
+        if (!SEG || len > 0) accumulate_points<DT, FT, CB, SUB, SEG, PPW_RT>(p, start, len, s, acc);
         const int bev = __builtin_amdgcn_readlane(cells, 1);
         fold_slots<E>(red[wv], acc, s, C, [&](int q, f32x4 sum) {
             if (FT == kE4M3) sum *= scale;
@@ -561,14 +616,13 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
             for (int e = 0; e < E; ++e) acc[e] = 0.f;
             if (lo < hi) {
                 if constexpr (LST > 0) {
-                    accumulate_points<DT, FT, CB, SUB, SEG, LST, LBATCH>(p, start + lo, hi - lo, s, acc,
-                                                                 (lds_char *)(__attribute__((address_space(3))) void *)red[wv]);
-                } else if constexpr (SUB_LP == SUB) {
-                    accumulate_points<DT, FT, CB, SUB, SEG>(p, start + lo, hi - lo, ss, acc);
+                    accumulate_points<DT, FT, CB, SUB, SEG, PPW_RT, LST>(
+                        p, start + lo, hi - lo, s, acc,
+                        (lds_char *)(__attribute__((address_space(3))) void *)red[wv]);
                 } else if (split) {
-                    accumulate_points<DT, FT, CB, SUB_LP, SEG>(p, start + lo, hi - lo, sp, acc);
+                    accumulate_points<DT, FT, CB, SUB_LP, SEG, PPW_PART_RT>(p, start + lo, hi - lo, sp, acc);
                 } else {
-                    accumulate_points<DT, FT, CB, SUB, SEG>(p, start + lo, hi - lo, s, acc);
+                    accumulate_points<DT, FT, CB, SUB, SEG, PPW_RT>(p, start + lo, hi - lo, s, acc);
                 }
             }
             fold_slots<E>(red[wv], acc, ss, Cw, [&](int q, f32x4 sum) {

@@ -64,6 +64,12 @@ typedef enum bevpool_dtype {
     BEVPOOL_BF16 = 3   /* output type of bevpool_forward_ex only */
 } bevpool_dtype;
 
+/* Largest feature table (or segment-reduce table) in bytes, 2^32 - 4096.
+ * Rows are addressed by 32-bit byte offsets from the table base; the kernels
+ * keep the top 4 KB of that range for the slots of a batch that hold no
+ * point, which read as zeros. */
+#define BEVPOOL_MAX_TABLE_BYTES 4294963200u
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *bevpool_status_string(int status);
 
@@ -144,8 +150,9 @@ int bevpool_build_map(const int32_t *point_cell, int32_t n_img, int32_t D, int32
  *       indices outside depth / feat / out are undefined behaviour.
  *   out [n_cells, C] fp32 (device, 16-byte aligned), overwritten.
  * Sizes: n_cells*C and n_feat_rows*C below 2^31 elements, n_depth below 2^31,
- *   and the feature table below 4 GiB (n_feat_rows*C*element bytes < 2^32;
- *   this binds only for F32 features); else BEVPOOL_ERR_OVERFLOW.
+ *   and the feature table at most BEVPOOL_MAX_TABLE_BYTES (n_feat_rows*C*
+ *   element bytes; this binds for F32 features, and for F16 ones only within
+ *   4 KB of 2^32 bytes); else BEVPOOL_ERR_OVERFLOW.
  * Asynchronous: enqueues on `stream` and returns; never synchronises or
  * allocates, so it may be captured into a HIP graph.  One kernel launch, or
  * several in stream order for more than 2^24 intervals.
@@ -212,7 +219,8 @@ int bevpool_forward_ex(const void *depth, int32_t depth_dtype, int64_t n_depth,
  *       non-decreasing, offsets[n_segments] <= n_points.  The kernel trusts
  *       them (values outside the arrays are undefined behaviour).
  *   out [n_segments, C] fp32 (device, 16-byte aligned), overwritten.
- * Sizes: n_segments*C and n_rows*C below 2^31, table below 4 GiB.
+ * Sizes: n_segments*C and n_rows*C below 2^31, table at most
+ * BEVPOOL_MAX_TABLE_BYTES.
  * Asynchronous, no allocation.  n_segments == 0 is a no-op.  Errors:
  * INVALID_ARG, UNSUPPORTED, OVERFLOW, HIP.
  */

@@ -34,6 +34,12 @@ def test_header_declares_the_boundary():
         assert required in names
 
 
+def test_table_limit_matches_header():
+    with open(os.path.join(os.path.dirname(dws.library_path()), "..", "include", "bevpool.h")) as f:
+        m = re.search(r"#define BEVPOOL_MAX_TABLE_BYTES (\d+)u", f.read())
+    assert m and int(m.group(1)) == dws.MAX_TABLE_BYTES == 2 ** 32 - 4096
+
+
 def test_every_declared_symbol_is_exported(lib):
     handle = ctypes.CDLL(dws.library_path())
     for name in declared_functions():
@@ -84,6 +90,8 @@ def _fwd(lib, **kw):
     (dict(n_cells=1 << 26, C=64), -3),          # n_cells * C >= 2^31
     (dict(rows=1 << 26, C=64), -3),
     (dict(ddt=dws.F32, fdt=dws.F32, rows=(1 << 24) + 1, C=64), -3),   # fp32 table of 4 GiB + 256 B
+    (dict(ddt=dws.F32, fdt=dws.F32, rows=16777201, C=64), -3),        # 256 B over the table limit
+    (dict(rows=8388601, C=256), -3),            # fp16 table 512 B over the limit, rows*C < 2^31
     (dict(out=FAKE + 4), -1),                   # misaligned output
     (dict(feat=FAKE + 8), -1),                  # misaligned features
 ])
@@ -161,6 +169,7 @@ def test_baseline_rejects(lib):
     (dict(C=12), -2),
     (dict(n_seg=1 << 26, C=64), -3),
     (dict(wdt=dws.F32, tdt=dws.F32, rows=1 << 24, C=64), -3),          # fp32 table of 4 GiB
+    (dict(wdt=dws.F32, tdt=dws.F32, rows=16777201, C=64), -3),         # 256 B over the table limit
     (dict(out=FAKE + 4), -1),
 ])
 def test_segment_reduce_rejects(lib, kw, code):

@@ -1,8 +1,8 @@
 """GPU parity at the size limits of the C ABI.
 
-* Feature tables just under the 4 GiB byte-offset limit (and under 2^31
-  elements), with the gathered rows at the top of the table, so the kernel's
-  32-bit unsigned row offsets run up to their largest values.
+* Feature tables at the byte limit of the C ABI (2^32 - 4096 bytes, and
+  under 2^31 elements), with the gathered rows at the top of the table, so
+  the kernel's 32-bit unsigned row offsets run up to their largest values.
 * An output of n_cells*C just under 2^31 elements (8.6 GB of fp32), with an
   occupied cell every 64 cells plus the first and the last cell, so every
   element is written (checked against a NaN fill) and the empty ones are 0.
@@ -55,7 +55,7 @@ LARGE_TABLES = [("f16", 80), ("f32", 64), ("e4m3", 512)]
 @pytest.mark.parametrize("feat_dtype,C", LARGE_TABLES, ids=[f"{a}-C{b}" for a, b in LARGE_TABLES])
 def test_forward_largest_feature_table(feat_dtype, C):
     eb = {"f32": 4, "f16": 2, "e4m3": 1}[feat_dtype]
-    n_rows = min(INT32_MAX // C, (2 ** 32 - 1) // (C * eb))
+    n_rows = min(INT32_MAX // C, dws.MAX_TABLE_BYTES // (C * eb))
     say(f"[largest table {feat_dtype} C={C}] rows={n_rows} bytes={n_rows * C * eb}")
     rng = np.random.default_rng(41)
     # rows used: the top 200 of the table and 100 elsewhere
