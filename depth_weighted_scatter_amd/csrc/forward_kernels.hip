@@ -381,6 +381,29 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
         const_cast<char *>(feat), 0, int(kEmptySlotOffset), kRawBufferWord3);
     int row0, didx0;
     load_indices<SEG>(p, t0, min(BATCH, n), s.lane, row0, didx0);
+    if constexpr (ZERO) {
+        if (n <= ROUND) {
+            // One batch of one round (most short intervals: 80 % have 13-18
+            // points at C=80): every slot group is requested unguarded (the
+            // empty ones read zeros) and no next batch exists, so the round
+            // carries no scalar bookkeeping.
+            const bool live = s.lane < n;
+            const int my_row = int(live ? uint32_t(row0 * s.row_G + s.coff) * uint32_t(CB)
+                                        : kEmptySlotOffset);
+            DRaw draw = SEG ? DRaw(0) : depth[didx0];
+            V v[SUB];
+#pragma unroll
+            for (int u = 0; u < SUB; ++u)
+                v[u] = load_chunk<CB>(rows_rsrc, uint32_t(__shfl(my_row, (u * s.PPW + s.g) & (kWave - 1))) +
+                                                     uint32_t(s.k * CB));
+            if (SEG) draw = depth ? depth[didx0] : DRaw(1);
+            const float my_d = live ? static_cast<float>(draw) : 0.f;
+#pragma unroll
+            for (int u = 0; u < SUB; ++u)
+                Accum<FT, CB>::run(acc, __shfl(my_d, (u * s.PPW + s.g) & (kWave - 1)), v[u]);
+            return;
+        }
+    }
     for (int base = 0; base < n; base += BATCH) {
         const int nb = min(BATCH, n - base);
         const bool more = base + BATCH < n;                // wave-uniform
