@@ -358,19 +358,20 @@ __device__ inline typename ChunkVec<CB>::type load_chunk(__amdgpu_buffer_rsrc_t 
 // points (ZERO), a batch is a whole number of rounds, so a slot's point index
 // never wraps past lane 63, and the slots without a point read a zero row
 // (kEmptySlotOffset) with weight zero: every lane accumulates without a
-// branch, exactly (0 * 0 adds +0 whatever the table holds).  Otherwise
-// (PPWC == 0: G known at run time; rounds over 64 points; LDS staging) the
-// lanes past the batch repeat its last point and empty slots are skipped by
-// exec mask.  Only wave-uniform guards branch in either case.
+// branch, exactly (0 * 0 adds +0 whatever the table holds).  Staged loads
+// past the table write zeros to LDS the same way.  Otherwise (PPWC == 0: G
+// known at run time; rounds over 64 points; staged rounds under 48 points,
+// which measured faster in 64-point batches than in whole rounds) the lanes
+// past the batch repeat its last point and empty slots are skipped by exec
+// mask.  Only wave-uniform guards branch in either case.
 template <int DT, int FT, int CB, int SUB, bool SEG, int PPWC, int LST = 0>
 __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, const Slots &s,
                                          float *acc, lds_char *stage = nullptr)
 {
     constexpr int ROUND = (SUB + LST) * (PPWC > 0 ? PPWC : kWave);
-    constexpr bool ZERO = PPWC > 0 && ROUND <= kWave && LST == 0;
+    constexpr bool ZERO = PPWC > 0 && ROUND <= kWave && (LST == 0 || ROUND >= 48);
     // Staged rounds of 48 or more points take batches of one round, so no
-    // round trip is spent on a batch's short remainder (36-point rounds
-    // measured faster with 64-point batches).
+    // round trip is spent on a batch's short remainder.
     constexpr int BATCH = ZERO ? kWave / ROUND * ROUND
                                : LST > 0 && ROUND >= 48 && ROUND <= kWave ? ROUND : kWave;
     using V = typename ChunkVec<CB>::type;
@@ -382,7 +383,7 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
     int row0, didx0;
     load_indices<SEG>(p, t0, min(BATCH, n), s.lane, row0, didx0);
     if constexpr (ZERO) {
-        if (n <= ROUND) {
+        if (LST == 0 && n <= ROUND) {                 // (staged rounds take the loop)
             // One batch of one round (most short intervals: 80 % have 13-18
             // points at C=80): every slot group is requested unguarded (the
             // empty ones read zeros) and no next batch exists, so the round
@@ -433,11 +434,18 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
             // further rows of the round go straight to LDS: lane i's 16 bytes
             // of staged instruction j at stage + 1024 j + 16 i
 #pragma unroll
-            for (int u = SUB; u < SUB + LST; ++u)
-                if (s0 + u * s.PPW < nb)
-                    __builtin_amdgcn_global_load_lds(
-                        (const void *)(feat + uint32_t(rows[u] + s.k) * uint32_t(CB)),
-                        (__attribute__((address_space(3))) void *)(stage + (u - SUB) * 1024), 16, 0, 0);
+            for (int u = SUB; u < SUB + LST; ++u) {
+                if (s0 + u * s.PPW < nb) {
+                    if constexpr (ZERO)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rows_rsrc, (__attribute__((address_space(3))) void *)(stage + (u - SUB) * 1024), 16,
+                            uint32_t(rows[u]) + uint32_t(s.k * CB), 0, 0, 0);
+                    else
+                        __builtin_amdgcn_global_load_lds(
+                            (const void *)(feat + uint32_t(rows[u] + s.k) * uint32_t(CB)),
+                            (__attribute__((address_space(3))) void *)(stage + (u - SUB) * 1024), 16, 0, 0);
+                }
+            }
             if (s0 == 0) {
                 const bool weighted = !SEG || depth;              // segments may be unweighted
                 if (SEG) draw = weighted ? depth[didx0] : DRaw(1);
@@ -465,7 +473,7 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
                 if (s0 + u * s.PPW < nb) {
                     typedef __attribute__((address_space(3))) const V lds_v;
                     const V x = *reinterpret_cast<lds_v *>(stage + (u - SUB) * 1024 + s.lane * 16);
-                    if (s.ok && s0 + u * s.PPW + s.g < nb) Accum<FT, CB>::run(acc, ds[u], x);
+                    if (ZERO || (s.ok && s0 + u * s.PPW + s.g < nb)) Accum<FT, CB>::run(acc, ds[u], x);
                 }
             }
         }
