@@ -126,8 +126,8 @@ int validate_forward(const void *depth, int32_t depth_dtype, int64_t n_depth, co
                          (depth_dtype == BEVPOOL_F16 && feat_dtype == BEVPOOL_F16) ||
                          (depth_dtype == BEVPOOL_F16 && feat_dtype == BEVPOOL_FP8_E4M3);
     if (!pair_ok || fe == 0) return BEVPOOL_ERR_UNSUPPORTED;
-    // a row is split into 16-byte lane chunks (8-byte ones for e4m3 rows of
-    // up to 512 bytes), at most 64 per row
+    // a row is split into 16-byte lane chunks (the kernels may take 8-byte
+    // ones for e4m3 rows of up to 512 bytes), at most 64 per row
     const int64_t row_bytes = int64_t(C) * fe;
     const bool e4m3_small = !tiles16 && feat_dtype == BEVPOOL_FP8_E4M3 && row_bytes <= 512;
     if (row_bytes % (e4m3_small ? 8 : 16) != 0 || row_bytes > 1024) return BEVPOOL_ERR_UNSUPPORTED;

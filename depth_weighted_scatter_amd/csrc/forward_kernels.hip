@@ -10,8 +10,8 @@
 // arrays carry explicit indices so nothing is divided at run time.
 //
 // CDNA4 mapping (our design, not the article's):
-//   * A feature row is split into G chunks of 16 bytes (8 bytes for e4m3 rows
-//     up to 512 bytes); lane (g, k) = g*G + k loads chunk k of point slot g,
+//   * A feature row is split into G chunks of 16 bytes (8 bytes for narrow
+//     e4m3 rows); lane (g, k) = g*G + k loads chunk k of point slot g,
 //     so one wave instruction gathers PPW = 64/G rows (C=80 fp16 or e4m3:
 //     G=10, six rows per instruction).  Row loads are raw buffer loads with a
 //     32-bit per-lane byte offset; a slot that holds no point reads at an
@@ -97,8 +97,9 @@ constexpr int kPartMin = 384;    // segments longer than this are split by chann
 constexpr int kMaxShortBlocks = 1 << 22;
 constexpr int64_t kContiguousTableBytes = int64_t(8) << 20;   // two XCD L2s
 
-// A lane's share of a feature row: CB bytes (16, or 8 for e4m3 rows up to
-// 512 bytes, which keeps e4m3 on the same ten-lane row geometry as fp16).
+// A lane's share of a feature row: CB bytes (16, or 8 for e4m3 rows under
+// 256 bytes -- 128 for segments -- which keeps them on the same row geometry
+// as fp16 rows of the same channel count; dispatch() picks it).
 template <int CB> struct ChunkVec;
 template <> struct ChunkVec<16> { using type = u32x4; };
 template <> struct ChunkVec<8> { using type = u32x2; };
@@ -715,6 +716,15 @@ void launch_g(FwdParams p, int n_short, size_t lds, hipStream_t s)
     }
 }
 
+// Chunk counts with a kernel of their own (others take the run-time-G one).
+// e4m3 rows only arrive in 8-byte chunks up to 248 bytes and in 16-byte
+// chunks from 128 bytes (segments) or 256 bytes (BEV); see dispatch().
+template <int FT, int CB, bool SEG>
+constexpr bool compiled_g(int g)
+{
+    return FT != kE4M3 || (CB == 8 ? g <= 20 : g >= (SEG ? 8 : 16));
+}
+
 template <int DT, int FT, int CB, bool SEG, int OD>
 hipError_t launch_typed(FwdParams p, hipStream_t s)
 {
@@ -726,20 +736,17 @@ hipError_t launch_typed(FwdParams p, hipStream_t s)
     p.xcd_run = !SEG && p.table_bytes > kContiguousTableBytes ? (short_blocks + 7) / 8 : 1;
     const int n_short = p.xcd_run == 1 ? short_blocks : 8 * p.xcd_run;
     const size_t lds = size_t(kWavesPerBlock) * p.C * sizeof(float);
-    if constexpr (FT == kE4M3 && CB == 16) {
-        // e4m3 rows take 16-byte chunks only past 512 bytes (33 chunks or more)
-        if (p.chunks == 64) launch_g<DT, FT, CB, 64, SEG, OD>(p, n_short, lds, s);
-        else launch_g<DT, FT, CB, 0, SEG, OD>(p, n_short, lds, s);
-    } else {
-#define BEVPOOL_CASE(GV) \
-    case GV: launch_g<DT, FT, CB, GV, SEG, OD>(p, n_short, lds, s); break;
-        switch (p.chunks) {
-            BEVPOOL_CASE(1) BEVPOOL_CASE(2) BEVPOOL_CASE(4) BEVPOOL_CASE(5) BEVPOOL_CASE(8)
-            BEVPOOL_CASE(10) BEVPOOL_CASE(16) BEVPOOL_CASE(20) BEVPOOL_CASE(32) BEVPOOL_CASE(64)
-        default: launch_g<DT, FT, CB, 0, SEG, OD>(p, n_short, lds, s); break;
-        }
-#undef BEVPOOL_CASE
+#define BEVPOOL_CASE(GV)                                                              \
+    case GV:                                                                          \
+        if constexpr (compiled_g<FT, CB, SEG>(GV)) launch_g<DT, FT, CB, GV, SEG, OD>(p, n_short, lds, s); \
+        else launch_g<DT, FT, CB, 0, SEG, OD>(p, n_short, lds, s);                    \
+        break;
+    switch (p.chunks) {
+        BEVPOOL_CASE(1) BEVPOOL_CASE(2) BEVPOOL_CASE(4) BEVPOOL_CASE(5) BEVPOOL_CASE(8)
+        BEVPOOL_CASE(10) BEVPOOL_CASE(16) BEVPOOL_CASE(20) BEVPOOL_CASE(32) BEVPOOL_CASE(64)
+    default: launch_g<DT, FT, CB, 0, SEG, OD>(p, n_short, lds, s); break;
     }
+#undef BEVPOOL_CASE
     return hipGetLastError();
 }
 
@@ -767,7 +774,12 @@ hipError_t dispatch(const FwdParams &p, hipStream_t s)
         return launch_out<kF16, kF16, 16, SEG>(q, s);
     }
     if (p.depth_dtype == kF16 && p.feat_dtype == kE4M3) {
-        if (row_bytes <= 8 * kWave) {
+        // 8-byte chunks keep narrow e4m3 rows on the fp16 row geometry (ten
+        // lanes a row at C=80); 16-byte chunks measured faster from 256-byte
+        // rows (C=256: -10 %) and, for segments, from 128-byte rows (-8 %),
+        // but slower below (C=80: +26 %, C=128: +19 %)
+        const int wide = SEG ? 128 : 256;
+        if (row_bytes <= 8 * kWave && (row_bytes < wide || row_bytes % 16 != 0)) {
             q.chunks = row_bytes / 8;
             return launch_out<kF16, kE4M3, 8, SEG>(q, s);
         }
