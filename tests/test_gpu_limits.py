@@ -191,6 +191,49 @@ def test_segment_reduce_more_segments_than_one_launch():
     assert (np.abs(got - ref) <= 1e-3 * ref_abs).all()
 
 
+SEG_TABLES = [("f32", 64), ("f16", 64), ("f16", 80), ("e4m3", 128)]
+
+
+@pytest.mark.parametrize("table_dtype,C", SEG_TABLES, ids=[f"{a}-C{b}" for a, b in SEG_TABLES])
+def test_segment_reduce_largest_table(table_dtype, C):
+    # a table at the byte limit, gathered at its top rows, through every row
+    # geometry of the segment kernel: fp32 C=64 (split by channels), fp16
+    # C=64 (staged rounds of 48 points), fp16 C=80 (staged rounds of 36
+    # points, masked slots), e4m3 C=128 (16-byte chunks)
+    eb = {"f32": 4, "f16": 2, "e4m3": 1}[table_dtype]
+    n_rows = min(INT32_MAX // C, dws.MAX_TABLE_BYTES // (C * eb))
+    say(f"[largest segment table {table_dtype} C={C}] rows={n_rows} bytes={n_rows * C * eb}")
+    rng = np.random.default_rng(43 + C)
+    used = np.unique(np.r_[np.arange(n_rows - 300, n_rows), rng.integers(0, n_rows, 100)])
+    vals = rng.standard_normal((used.size, C))
+    scale = 1.0
+    if table_dtype == "f32":
+        vals, tdt, wdt = vals.astype(np.float32), torch.float32, np.float32
+    elif table_dtype == "f16":
+        vals, tdt, wdt = vals.astype(np.float16), torch.float16, np.float16
+    else:
+        vals, scale = W.quantize_e4m3(vals.astype(np.float16))
+        tdt, wdt = torch.uint8, np.float16
+    lens = np.r_[rng.integers(0, 60, 40), [97, 400, 1500, 2000, 1, 0, 48, 49]]
+    offsets = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N = int(offsets[-1])
+    pick = rng.integers(0, used.size, N).astype(np.int32)
+    weights = rng.random(N).astype(wdt)
+    table = torch.zeros((n_rows, C), dtype=tdt, device=dev())
+    table[torch.from_numpy(used).to(dev())] = torch.from_numpy(vals).to(dev())
+    out = torch.full((lens.size, C), float("nan"), dtype=torch.float32, device=dev())
+    dws.bevpool_segment_reduce(to_gpu(weights), table, to_gpu(used[pick].astype(np.int32)),
+                               to_gpu(offsets), table_scale=scale, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    del table
+    torch.cuda.empty_cache()
+    ref, ref_abs = oracle.segment_reduce(weights, vals, table_dtype, scale, pick, offsets,
+                                         with_abs=True)        # rows renumbered densely
+    check_forward(got, ref, ref_abs, table_dtype, np.flatnonzero(lens > 0),
+                  f"segment table {table_dtype} C={C}")
+
+
 def test_build_map_largest_frustum():
     # n_img*D*H*W = 2^31 - 1, the largest frustum the map builder takes, with
     # kept points spread over it and packed into its last few thousand indices
