@@ -716,13 +716,14 @@ void launch_g(FwdParams p, int n_short, size_t lds, hipStream_t s)
     }
 }
 
-// Chunk counts with a kernel of their own (others take the run-time-G one).
-// e4m3 rows only arrive in 8-byte chunks up to 248 bytes and in 16-byte
-// chunks from 128 bytes (segments) or 256 bytes (BEV); see dispatch().
+// Chunk counts with a kernel of their own (others take the run-time-G one,
+// which measured 23-25 % slower at C=48, 96 and 192 fp16 before 6, 12 and 24
+// got theirs).  e4m3 rows only arrive in 8-byte chunks up to 248 bytes and in
+// 16-byte chunks from 128 bytes (segments) or 256 bytes (BEV); see dispatch().
 template <int FT, int CB, bool SEG>
 constexpr bool compiled_g(int g)
 {
-    return FT != kE4M3 || (CB == 8 ? g <= 20 : g >= (SEG ? 8 : 16));
+    return FT != kE4M3 || (CB == 8 ? g < 32 : g >= (SEG ? 8 : 16));
 }
 
 template <int DT, int FT, int CB, bool SEG, int OD>
@@ -743,7 +744,8 @@ hipError_t launch_typed(FwdParams p, hipStream_t s)
         break;
     switch (p.chunks) {
         BEVPOOL_CASE(1) BEVPOOL_CASE(2) BEVPOOL_CASE(4) BEVPOOL_CASE(5) BEVPOOL_CASE(8)
-        BEVPOOL_CASE(10) BEVPOOL_CASE(16) BEVPOOL_CASE(20) BEVPOOL_CASE(32) BEVPOOL_CASE(64)
+        BEVPOOL_CASE(6) BEVPOOL_CASE(10) BEVPOOL_CASE(12) BEVPOOL_CASE(16) BEVPOOL_CASE(20)
+        BEVPOOL_CASE(24) BEVPOOL_CASE(32) BEVPOOL_CASE(64)
     default: launch_g<DT, FT, CB, 0, SEG, OD>(p, n_short, lds, s); break;
     }
 #undef BEVPOOL_CASE

@@ -143,11 +143,13 @@ def _make_inputs(rng, n_img, D, H, Wd, C, feat_dtype):
     return depth.astype(np.float16), q, float(scale)
 
 
-CHANNEL_CASES = [("f32", 4), ("f32", 8), ("f32", 12), ("f32", 80), ("f32", 128), ("f32", 256),
-                 ("f16", 8), ("f16", 24), ("f16", 64), ("f16", 80), ("f16", 96), ("f16", 128),
-                 ("f16", 256), ("f16", 512),
-                 ("e4m3", 8), ("e4m3", 16), ("e4m3", 40), ("e4m3", 48), ("e4m3", 80),
-                 ("e4m3", 128), ("e4m3", 256), ("e4m3", 512), ("e4m3", 528), ("e4m3", 1024)]
+CHANNEL_CASES = [("f32", 4), ("f32", 8), ("f32", 12), ("f32", 24), ("f32", 48), ("f32", 80),
+                 ("f32", 96), ("f32", 128), ("f32", 256),
+                 ("f16", 8), ("f16", 24), ("f16", 48), ("f16", 64), ("f16", 80), ("f16", 96),
+                 ("f16", 128), ("f16", 192), ("f16", 256), ("f16", 512),
+                 ("e4m3", 8), ("e4m3", 16), ("e4m3", 40), ("e4m3", 48), ("e4m3", 80), ("e4m3", 96),
+                 ("e4m3", 128), ("e4m3", 192), ("e4m3", 256), ("e4m3", 384), ("e4m3", 512),
+                 ("e4m3", 528), ("e4m3", 1024)]
 
 
 @pytest.mark.parametrize("feat_dtype,C", CHANNEL_CASES, ids=[f"{a}-C{b}" for a, b in CHANNEL_CASES])
@@ -536,13 +538,15 @@ def test_segment_reduce_edge_cases(case):
     check_forward(got, ref, ref_abs, dtype, nonempty, case)
 
 
-# Long segments of unsplit rows (2, 4, 5, 8 or 10 chunks) take the long role
-# with staged row loads; rows of 16 or more chunks are split by channels.
+# Long segments of unsplit rows (2 to 12 chunks) take the long role with
+# staged row loads; rows of 16 or more chunks (a multiple of 4) are split by
+# channels.
 # Lengths sit around the long-role threshold (96), the 64-point index batches
 # a wave's quarter falls into, and the channel-split threshold (384).
 LONG_SEGMENT_ROWS = [("f32", 8), ("f32", 16), ("f32", 20), ("f32", 32), ("f32", 40),
                      ("f16", 16), ("f16", 32), ("f16", 40), ("f16", 64), ("f16", 80),
-                     ("f16", 128), ("f16", 256), ("e4m3", 80), ("e4m3", 128)]
+                     ("f16", 128), ("f16", 256), ("e4m3", 80), ("e4m3", 128), ("f32", 24),
+                     ("f16", 48), ("f16", 96), ("f16", 192), ("e4m3", 96), ("e4m3", 192)]
 
 
 @pytest.mark.parametrize("table_dtype,C", LONG_SEGMENT_ROWS,
