@@ -342,8 +342,8 @@ def main():
         print("--out-dtype applies to the owned kernel only", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: the pooled forward has no cross-GPU step in "
-              f"this build (asked for --gpus {args.gpus}).", file=sys.stderr)
+        print(f"bench.py runs on one GPU only: the pooled forward has no cross-GPU step "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
