@@ -509,7 +509,10 @@ __device__ inline void fold_slots(float *r, const float *acc, const Slots &s, in
 }
 
 // CB: bytes per lane chunk.  G_CT > 0: lanes per point (chunks per row)
-// fixed at compile time; G_CT == 0: p.chunks.  OD: the output type, fixed at
+// fixed at compile time; G_CT < 0: p.chunks lanes per point and -G_CT points
+// per wave (the rows of other widths keep the compile-time wave geometry:
+// unrolled rounds, zero-row padding, the one-round path); G_CT == 0: both
+// from p.chunks.  OD: the output type, fixed at
 // compile time so the stores and zero fills carry no type branches (they
 // measured 1-2 % of the call in scalar instructions).
 //
@@ -520,15 +523,16 @@ template <int DT, int FT, int CB, int G_CT, bool SEG, int OD>
 __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
 {
     constexpr int E = CB / elem_bytes(FT);   // row elements per lane
-    constexpr int PPW_CT = G_CT > 0 ? kWave / G_CT : 1;
-    constexpr int PPW_RT = G_CT > 0 ? PPW_CT : 0;   // 0: known at run time only
+    constexpr int PPW_CT = G_CT > 0 ? kWave / G_CT : G_CT < 0 ? -G_CT : 1;
+    constexpr int PPW_RT = G_CT != 0 ? PPW_CT : 0;   // 0: known at run time only
     // rows in flight per lane: about kRoundPoints points per request round,
     // which keeps the common kernels near 64 VGPRs (up to eight waves per SIMD);
     // rows of 16 or more chunks (at most four points per instruction) take
     // four instructions per round, which measured faster than more rows in
     // flight at half the occupancy (C = 128 and 256)
-    constexpr int SUB_RAW = G_CT > 0 ? (kRoundPoints + PPW_CT - 1) / PPW_CT : 4;
-    constexpr int SUB = G_CT >= 16 ? (SUB_RAW > 4 ? 4 : SUB_RAW)
+    constexpr int SUB_RAW = G_CT != 0 ? (kRoundPoints + PPW_CT - 1) / PPW_CT : 4;
+    constexpr bool WIDE = G_CT >= 16 || (G_CT < 0 && PPW_CT <= 4);   // 13 or more chunks
+    constexpr int SUB = WIDE ? (SUB_RAW > 4 ? 4 : SUB_RAW)
                                    : SUB_RAW > 8 ? 8 : (SUB_RAW > 5 && E == 16 ? 5 : SUB_RAW);
     // A channel part of a long segment (segment reductions, rows split by
     // channels) mostly misses L2 (tables larger than it), so its waves request
@@ -554,7 +558,7 @@ __global__ __launch_bounds__(kBlock) void bev_pool_fwd(FwdParams p)
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     Slots s;
     s.G = G_CT > 0 ? G_CT : p.chunks;
-    s.PPW = G_CT > 0 ? PPW_CT : kWave / s.G;
+    s.PPW = G_CT != 0 ? PPW_CT : kWave / s.G;
     s.g = lane / s.G;
     s.k = lane - s.g * s.G;
     s.lane = lane;
@@ -726,6 +730,25 @@ constexpr bool compiled_g(int g)
     return FT != kE4M3 || (CB == 8 ? g < 32 : g >= (SEG ? 8 : 16));
 }
 
+// Rows whose chunk count has no kernel of its own: the kernel for their
+// points per wave (64 / chunks: 1, 2, 3, 4, 5, 7, 9 or 21 for the counts
+// that reach here).  A run-time wave geometry measured 23-25 % slower.
+template <int DT, int FT, int CB, bool SEG, int OD>
+void launch_ppw(FwdParams p, int n_short, size_t lds, hipStream_t s)
+{
+    switch (kWave / p.chunks) {
+    case 1: launch_g<DT, FT, CB, -1, SEG, OD>(p, n_short, lds, s); break;
+    case 2: launch_g<DT, FT, CB, -2, SEG, OD>(p, n_short, lds, s); break;
+    case 3: launch_g<DT, FT, CB, -3, SEG, OD>(p, n_short, lds, s); break;
+    case 4: launch_g<DT, FT, CB, -4, SEG, OD>(p, n_short, lds, s); break;
+    case 5: launch_g<DT, FT, CB, -5, SEG, OD>(p, n_short, lds, s); break;
+    case 7: launch_g<DT, FT, CB, -7, SEG, OD>(p, n_short, lds, s); break;
+    case 9: launch_g<DT, FT, CB, -9, SEG, OD>(p, n_short, lds, s); break;
+    case 21: launch_g<DT, FT, CB, -21, SEG, OD>(p, n_short, lds, s); break;
+    default: launch_g<DT, FT, CB, 0, SEG, OD>(p, n_short, lds, s); break;
+    }
+}
+
 template <int DT, int FT, int CB, bool SEG, int OD>
 hipError_t launch_typed(FwdParams p, hipStream_t s)
 {
@@ -740,13 +763,13 @@ hipError_t launch_typed(FwdParams p, hipStream_t s)
 #define BEVPOOL_CASE(GV)                                                              \
     case GV:                                                                          \
         if constexpr (compiled_g<FT, CB, SEG>(GV)) launch_g<DT, FT, CB, GV, SEG, OD>(p, n_short, lds, s); \
-        else launch_g<DT, FT, CB, 0, SEG, OD>(p, n_short, lds, s);                    \
+        else launch_ppw<DT, FT, CB, SEG, OD>(p, n_short, lds, s);                     \
         break;
     switch (p.chunks) {
         BEVPOOL_CASE(1) BEVPOOL_CASE(2) BEVPOOL_CASE(4) BEVPOOL_CASE(5) BEVPOOL_CASE(8)
         BEVPOOL_CASE(6) BEVPOOL_CASE(10) BEVPOOL_CASE(12) BEVPOOL_CASE(16) BEVPOOL_CASE(20)
         BEVPOOL_CASE(24) BEVPOOL_CASE(32) BEVPOOL_CASE(64)
-    default: launch_g<DT, FT, CB, 0, SEG, OD>(p, n_short, lds, s); break;
+    default: launch_ppw<DT, FT, CB, SEG, OD>(p, n_short, lds, s); break;
     }
 #undef BEVPOOL_CASE
     return hipGetLastError();

@@ -17,9 +17,9 @@ from gpu_util import TOL, dev, gpu_map, map_to_numpy, assert_maps_equal, say, to
 
 pytestmark = pytest.mark.gpu
 
-C_CHOICES = {"f32": [4, 8, 12, 24, 32, 48, 80, 96, 128, 256],
-             "f16": [8, 16, 24, 48, 80, 96, 128, 192, 256, 512],
-             "e4m3": [8, 16, 40, 80, 96, 128, 192, 256, 384, 512, 528, 1024]}
+C_CHOICES = {"f32": [4, 8, 12, 24, 28, 32, 48, 60, 80, 96, 128, 256],
+             "f16": [8, 16, 24, 48, 56, 72, 80, 88, 96, 128, 152, 192, 200, 256, 320, 512],
+             "e4m3": [8, 16, 40, 72, 80, 96, 128, 192, 200, 256, 264, 384, 512, 528, 1024]}
 OUT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 UNIT = {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
 TINY = {"f32": 0.0, "f16": 2.0 ** -25, "bf16": 2.0 ** -134}

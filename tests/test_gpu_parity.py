@@ -143,13 +143,16 @@ def _make_inputs(rng, n_img, D, H, Wd, C, feat_dtype):
     return depth.astype(np.float16), q, float(scale)
 
 
-CHANNEL_CASES = [("f32", 4), ("f32", 8), ("f32", 12), ("f32", 24), ("f32", 48), ("f32", 80),
-                 ("f32", 96), ("f32", 128), ("f32", 256),
-                 ("f16", 8), ("f16", 24), ("f16", 48), ("f16", 64), ("f16", 80), ("f16", 96),
-                 ("f16", 128), ("f16", 192), ("f16", 256), ("f16", 512),
-                 ("e4m3", 8), ("e4m3", 16), ("e4m3", 40), ("e4m3", 48), ("e4m3", 80), ("e4m3", 96),
-                 ("e4m3", 128), ("e4m3", 192), ("e4m3", 256), ("e4m3", 384), ("e4m3", 512),
-                 ("e4m3", 528), ("e4m3", 1024)]
+# Chunk counts with a kernel of their own and others (7, 9, 11, 15, 19, 25,
+# 33, 40 chunks: kernels with the points per wave fixed instead).
+CHANNEL_CASES = [("f32", 4), ("f32", 8), ("f32", 12), ("f32", 24), ("f32", 28), ("f32", 48),
+                 ("f32", 60), ("f32", 80), ("f32", 96), ("f32", 128), ("f32", 256),
+                 ("f16", 8), ("f16", 24), ("f16", 48), ("f16", 56), ("f16", 64), ("f16", 72),
+                 ("f16", 80), ("f16", 88), ("f16", 96), ("f16", 120), ("f16", 128), ("f16", 152),
+                 ("f16", 192), ("f16", 200), ("f16", 256), ("f16", 320), ("f16", 512),
+                 ("e4m3", 8), ("e4m3", 16), ("e4m3", 40), ("e4m3", 48), ("e4m3", 72), ("e4m3", 80),
+                 ("e4m3", 96), ("e4m3", 128), ("e4m3", 192), ("e4m3", 200), ("e4m3", 256),
+                 ("e4m3", 264), ("e4m3", 384), ("e4m3", 512), ("e4m3", 528), ("e4m3", 1024)]
 
 
 @pytest.mark.parametrize("feat_dtype,C", CHANNEL_CASES, ids=[f"{a}-C{b}" for a, b in CHANNEL_CASES])
@@ -546,7 +549,8 @@ def test_segment_reduce_edge_cases(case):
 LONG_SEGMENT_ROWS = [("f32", 8), ("f32", 16), ("f32", 20), ("f32", 32), ("f32", 40),
                      ("f16", 16), ("f16", 32), ("f16", 40), ("f16", 64), ("f16", 80),
                      ("f16", 128), ("f16", 256), ("e4m3", 80), ("e4m3", 128), ("f32", 24),
-                     ("f16", 48), ("f16", 96), ("f16", 192), ("e4m3", 96), ("e4m3", 192)]
+                     ("f16", 48), ("f16", 96), ("f16", 192), ("e4m3", 96), ("e4m3", 192),
+                     ("f16", 56), ("f16", 88), ("f16", 200), ("e4m3", 72)]
 
 
 @pytest.mark.parametrize("table_dtype,C", LONG_SEGMENT_ROWS,
