@@ -9,6 +9,11 @@ and batch sizes of each row geometry and past the one-wave and channel-split
 limits.  The oracle's fp64 sums give the expected NaN / +Inf / -Inf pattern
 (IEEE arithmetic decides it, whatever the summation order); every other
 element must match the oracle to the usual scaled tolerance.
+
+OCP e4m3 has no infinities: its rows carry the NaN codes instead (0x7F where
+the other types hold +Inf, 0xFF where they hold -Inf), so an e4m3 interval's
+first or last point reaches its cell as NaN, and an Inf weight turns every
+finite channel of its point into +Inf.
 """
 import numpy as np
 import pytest
@@ -55,6 +60,18 @@ def _inputs(C, np_dtype, seed):
     return lens, starts, rows, w
 
 
+def _rows_of(dtype, rows):
+    """Rows in the feature type: fp16 / fp32 as they are; e4m3 as codes, with
+    the infinities replaced by the format's NaN codes."""
+    if dtype != "e4m3":
+        return rows
+    finite = np.where(np.isfinite(rows), rows, 1.0).astype(np.float32)
+    codes = torch.from_numpy(finite).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    codes[np.isposinf(rows)] = 0x7F
+    codes[np.isneginf(rows)] = 0xFF
+    return codes
+
+
 def _check(got, ref, ref_abs, dtype, label):
     for name, f in (("NaN", np.isnan), ("+Inf", np.isposinf), ("-Inf", np.isneginf)):
         a, b = f(got), f(ref)
@@ -68,14 +85,18 @@ def _check(got, ref, ref_abs, dtype, label):
 
 
 # (feature dtype, C): ten-chunk rows (6 points per instruction), 16-chunk
-# rows, five-chunk rows, fp32 16-chunk rows, 32-chunk rows
-GEOMETRIES = [("f16", 80), ("f16", 128), ("f16", 40), ("f32", 64), ("f16", 256)]
+# rows, five-chunk rows, fp32 16-chunk rows, 32-chunk rows, e4m3 rows of ten
+# 8-byte chunks and of sixteen 16-byte chunks (split by channels in segment
+# reductions)
+GEOMETRIES = [("f16", 80), ("f16", 128), ("f16", 40), ("f32", 64), ("f16", 256),
+              ("e4m3", 80), ("e4m3", 256)]
 
 
 @pytest.mark.parametrize("dtype,C", GEOMETRIES, ids=[f"{a}-C{b}" for a, b in GEOMETRIES])
 def test_forward_nonfinite_rows_and_weights(dtype, C):
-    np_dtype = np.float16 if dtype == "f16" else np.float32
+    np_dtype = np.float32 if dtype == "f32" else np.float16
     lens, starts, rows, w = _inputs(C, np_dtype, 70 + C)
+    rows = _rows_of(dtype, rows)
     n_iv = lens.size
     say(f"[nonfinite forward {dtype} C={C}] intervals={n_iv} N={rows.shape[0]}")
     # one cell per interval, every other cell empty
@@ -99,8 +120,9 @@ def test_forward_nonfinite_rows_and_weights(dtype, C):
 
 @pytest.mark.parametrize("dtype,C", GEOMETRIES, ids=[f"{a}-C{b}" for a, b in GEOMETRIES])
 def test_segment_reduce_nonfinite_rows_and_weights(dtype, C):
-    np_dtype = np.float16 if dtype == "f16" else np.float32
+    np_dtype = np.float32 if dtype == "f32" else np.float16
     lens, starts, rows, w = _inputs(C, np_dtype, 90 + C)
+    rows = _rows_of(dtype, rows)
     say(f"[nonfinite segments {dtype} C={C}] segments={lens.size} N={rows.shape[0]}")
     off = np.r_[starts, lens.sum()].astype(np.int32)
     idx = np.arange(rows.shape[0], dtype=np.int32)

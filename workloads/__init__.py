@@ -40,7 +40,8 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["WorkloadSpec", "Workload", "SPECS", "spec", "make_workload",
-           "make_random_cells", "describe", "BagSpec", "BAG_SPECS", "make_bags"]
+           "make_random_cells", "describe", "BagSpec", "BAG_SPECS", "make_bags",
+           "exact_values", "power_of_two_weights"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -163,6 +164,28 @@ def quantize_e4m3(x: np.ndarray):
     t = torch.from_numpy(xf * (448.0 / absmax)).clamp_(-448.0, 448.0)
     codes = t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
     return codes, np.float32(absmax / 448.0)
+
+
+def exact_values(rng: np.random.Generator, shape, dtype: str, lo: int = -8, hi: int = 8):
+    """Nonzero integers drawn uniformly from [lo, hi] without 0, stored as
+    float32 / float16, or as OCP e4m3 codes (dtype "e4m3": integers up to 16
+    in magnitude are exact in that format).  Returns (array, scale) with
+    scale 0.5 for e4m3 (a power of two) and 1.0 otherwise."""
+    import torch
+    choices = np.array([v for v in range(lo, hi + 1) if v != 0], dtype=np.float64)
+    x = choices[rng.integers(0, choices.size, size=shape)]
+    if dtype == "f32":
+        return x.astype(np.float32), 1.0
+    if dtype == "f16":
+        return x.astype(np.float16), 1.0
+    codes = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return codes, 0.5
+
+
+def power_of_two_weights(rng: np.random.Generator, n: int, dtype: str) -> np.ndarray:
+    """Weights drawn from {0.5, 1, 2} as float32 / float16 (exact in both)."""
+    w = np.array([0.5, 1.0, 2.0])[rng.integers(0, 3, size=n)]
+    return w.astype(np.float32 if dtype == "f32" else np.float16)
 
 
 def make_workload(k: int, seed: int = 0) -> Workload:
