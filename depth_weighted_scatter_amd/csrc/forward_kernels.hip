@@ -379,8 +379,15 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
     using DRaw = typename DepthT<DT>::type;
     const DRaw *depth = static_cast<const DRaw *>(p.depth);
     const char *feat = static_cast<const char *>(p.feat);
+    // Range of the raw buffer: segment indices come from the caller, so their
+    // rows are bounded by the real table size (an index past the table reads
+    // zeros rather than memory beyond it).  BEV maps come from
+    // bevpool_build_map; their kernels keep the constant bound, which the
+    // compiler folds (the table size as a kernel argument made it re-issue a
+    // descriptor word before every row load: six scalar instructions per wave).
     const __amdgpu_buffer_rsrc_t rows_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(feat), 0, int(kEmptySlotOffset), kRawBufferWord3);
+        const_cast<char *>(feat), 0, SEG ? int(uint32_t(p.table_bytes)) : int(kEmptySlotOffset),
+        kRawBufferWord3);
     int row0, didx0;
     load_indices<SEG>(p, t0, min(BATCH, n), s.lane, row0, didx0);
     if constexpr (ZERO) {
@@ -428,6 +435,8 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
                 if (s0 + u * s.PPW < nb) {
                     if constexpr (ZERO)
                         v[u] = load_chunk<CB>(rows_rsrc, uint32_t(rows[u]) + uint32_t(s.k * CB));
+                    else if constexpr (SEG)
+                        v[u] = load_chunk<CB>(rows_rsrc, uint32_t(rows[u] + s.k) * uint32_t(CB));
                     else
                         v[u] = *reinterpret_cast<const V *>(feat + uint32_t(rows[u] + s.k) * uint32_t(CB));
                 }
@@ -441,10 +450,10 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
                         __builtin_amdgcn_raw_ptr_buffer_load_lds(
                             rows_rsrc, (__attribute__((address_space(3))) void *)(stage + (u - SUB) * 1024), 16,
                             uint32_t(rows[u]) + uint32_t(s.k * CB), 0, 0, 0);
-                    else
-                        __builtin_amdgcn_global_load_lds(
-                            (const void *)(feat + uint32_t(rows[u] + s.k) * uint32_t(CB)),
-                            (__attribute__((address_space(3))) void *)(stage + (u - SUB) * 1024), 16, 0, 0);
+                    else   // (staged loads are segment mode only)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rows_rsrc, (__attribute__((address_space(3))) void *)(stage + (u - SUB) * 1024), 16,
+                            uint32_t(rows[u] + s.k) * uint32_t(CB), 0, 0, 0);
                 }
             }
             if (s0 == 0) {
