@@ -32,7 +32,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared",
-                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+                               "-Wall", "-Wextra", "-pthread", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -51,6 +51,10 @@ def _bind(path: str):
     lib.oracle_forward.restype = ctypes.c_int
     lib.oracle_forward.argtypes = [vp, ctypes.c_int, i64, vp, ctypes.c_int, i64, i64,
                                    ctypes.c_double, vp, vp, vp, i64, i64, dp, dp]
+    lib.oracle_forward_threads.restype = ctypes.c_int
+    lib.oracle_forward_threads.argtypes = [vp, ctypes.c_int, i64, vp, ctypes.c_int, i64, i64,
+                                           ctypes.c_double, vp, vp, vp, i64, vp, vp, i64, i64,
+                                           ctypes.c_int, dp, dp]
     lib.oracle_segment_reduce.restype = ctypes.c_int
     lib.oracle_segment_reduce.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64,
                                           ctypes.c_double, vp, vp, i64, dp, dp]
@@ -141,6 +145,35 @@ def forward(depth: np.ndarray, feat: np.ndarray, feat_dtype: str, feat_scale: fl
                             _ptr(out), _ptr(out_abs) if with_abs else None)
     if rc != 0:
         raise ValueError(f"oracle_forward failed ({rc})")
+    return (out, out_abs) if with_abs else out
+
+
+def forward_threads(depth: np.ndarray, feat: np.ndarray, feat_dtype: str, feat_scale: float,
+                    C: int, m: dict, n_cells: int, n_threads: int, with_abs: bool = False):
+    """forward() spread over n_threads host threads, each taking a contiguous
+    range of whole intervals of the map m (which must come from build_map:
+    intervals tile the points, one per cell).  Bitwise equal to forward()."""
+    lib = _load()
+    depth = np.ascontiguousarray(depth)
+    feat = np.ascontiguousarray(feat)
+    ddt = {np.dtype(np.float32): F32, np.dtype(np.float16): F16}[depth.dtype]
+    fdt = _DTYPE_CODE[feat_dtype]
+    expect = {F32: np.float32, F16: np.float16, E4M3: np.uint8}[fdt]
+    if feat.dtype != expect:
+        raise TypeError(f"feat dtype {feat.dtype} does not match {feat_dtype}")
+    arrs = {k: np.ascontiguousarray(m[k], np.int32)
+            for k in ("ranks_depth", "ranks_feat", "ranks_bev", "interval_starts",
+                      "interval_lengths")}
+    out = np.empty((n_cells, C), np.float64)
+    out_abs = np.empty((n_cells, C), np.float64) if with_abs else None
+    rc = lib.oracle_forward_threads(
+        _ptr(depth), ddt, depth.size, _ptr(feat), fdt, feat.size // C, C, float(feat_scale),
+        _ptr(arrs["ranks_depth"]), _ptr(arrs["ranks_feat"]), _ptr(arrs["ranks_bev"]),
+        arrs["ranks_bev"].size, _ptr(arrs["interval_starts"]), _ptr(arrs["interval_lengths"]),
+        arrs["interval_starts"].size, n_cells, int(n_threads),
+        _ptr(out), _ptr(out_abs) if with_abs else None)
+    if rc != 0:
+        raise ValueError(f"oracle_forward_threads failed ({rc})")
     return (out, out_abs) if with_abs else out
 
 

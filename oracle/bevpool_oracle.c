@@ -35,6 +35,7 @@
  * against torch.nn.functional.embedding_bag and against the forward itself.
  */
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -142,6 +143,48 @@ int oracle_build_map(const int32_t *point_cell, int64_t n_img, int64_t D,
     return 0;
 }
 
+/* The forward's operands, as passed to oracle_forward. */
+typedef struct {
+    const void *depth; int depth_dtype; int64_t n_depth;
+    const void *feat; int feat_dtype; int64_t n_feat_rows; int64_t C; double feat_scale;
+    const int32_t *ranks_depth, *ranks_feat, *ranks_bev;
+    int64_t n_cells;
+    double *out, *out_abs;
+} oracle_fwd_args;
+
+/* e4m3 values are dequantised with the per-tensor scale; other types not. */
+static double feat_scale_of(int feat_dtype, double feat_scale)
+{
+    return feat_dtype == ORACLE_E4M3 ? feat_scale : 1.0;
+}
+
+/* Adds the terms of points [t_lo, t_hi), in increasing t, into out (and
+ * out_abs).  Returns -1 on an index outside the stated sizes, else 0. */
+static int sum_points(const oracle_fwd_args *a, int64_t t_lo, int64_t t_hi)
+{
+    int64_t C = a->C;
+    double fscale = feat_scale_of(a->feat_dtype, a->feat_scale);
+    for (int64_t t = t_lo; t < t_hi; ++t) {
+        int64_t rd = a->ranks_depth[t], rf = a->ranks_feat[t], rb = a->ranks_bev[t];
+        if (rd < 0 || rd >= a->n_depth || rf < 0 || rf >= a->n_feat_rows || rb < 0 ||
+            rb >= a->n_cells)
+            return -1;
+        double d = load_value(a->depth, a->depth_dtype, rd);
+        for (int64_t c = 0; c < C; ++c) {
+            double term = d * (load_value(a->feat, a->feat_dtype, rf * C + c) * fscale);
+            a->out[rb * C + c] += term;
+            if (a->out_abs) a->out_abs[rb * C + c] += fabs(term);
+        }
+    }
+    return 0;
+}
+
+static int check_dtypes(int depth_dtype, int feat_dtype)
+{
+    return depth_dtype >= ORACLE_F32 && depth_dtype <= ORACLE_F16 &&
+           feat_dtype >= ORACLE_F32 && feat_dtype <= ORACLE_E4M3;
+}
+
 /*
  * The scatter-reduce itself, in double:
  *   out[ranks_bev[t], c] = sum over t (increasing) of
@@ -159,25 +202,93 @@ int oracle_forward(const void *depth, int depth_dtype, int64_t n_depth,
                    const int32_t *ranks_bev, int64_t n_points, int64_t n_cells,
                    double *out, double *out_abs)
 {
-    if (depth_dtype < ORACLE_F32 || depth_dtype > ORACLE_F16) return -1;
-    if (feat_dtype < ORACLE_F32 || feat_dtype > ORACLE_E4M3) return -1;
-    double fscale = feat_dtype == ORACLE_E4M3 ? feat_scale : 1.0;
-
+    if (!check_dtypes(depth_dtype, feat_dtype)) return -1;
+    oracle_fwd_args a = {depth, depth_dtype, n_depth, feat, feat_dtype, n_feat_rows, C,
+                         feat_scale, ranks_depth, ranks_feat, ranks_bev, n_cells, out, out_abs};
     memset(out, 0, (size_t)(n_cells * C) * sizeof(double));
     if (out_abs) memset(out_abs, 0, (size_t)(n_cells * C) * sizeof(double));
+    return sum_points(&a, 0, n_points);
+}
 
-    for (int64_t t = 0; t < n_points; ++t) {
-        int64_t rd = ranks_depth[t], rf = ranks_feat[t], rb = ranks_bev[t];
-        if (rd < 0 || rd >= n_depth || rf < 0 || rf >= n_feat_rows || rb < 0 || rb >= n_cells)
-            return -1;
-        double d = load_value(depth, depth_dtype, rd);
-        for (int64_t c = 0; c < C; ++c) {
-            double term = d * (load_value(feat, feat_dtype, rf * C + c) * fscale);
-            out[rb * C + c] += term;
-            if (out_abs) out_abs[rb * C + c] += fabs(term);
-        }
+/*
+ * The same sum spread over host threads, for timing the oracle on all host
+ * cores.  It takes the map's intervals as well, and requires what a map from
+ * oracle_build_map satisfies: the intervals tile [0, n_points) in order and
+ * their cells strictly increase, so no cell is split between intervals.
+ * Thread k takes a contiguous range of whole intervals: those that end at or
+ * before point n_points * (k + 1) / n_threads and were not taken by thread
+ * k - 1 (the last thread takes the rest), so every cell is summed by one
+ * thread over its points in increasing t -- the same operations in the same
+ * order as oracle_forward (the same sum_points), hence the same bits for any
+ * thread count.  Returns 0, or -1 when the map breaks that structure (or as
+ * oracle_forward), or -2 when a thread cannot be started.
+ */
+typedef struct {
+    const oracle_fwd_args *a;
+    int64_t t_lo, t_hi;
+    int status;
+} oracle_range;
+
+static void *sum_range(void *arg)
+{
+    oracle_range *r = (oracle_range *)arg;
+    r->status = sum_points(r->a, r->t_lo, r->t_hi);
+    return NULL;
+}
+
+int oracle_forward_threads(const void *depth, int depth_dtype, int64_t n_depth,
+                           const void *feat, int feat_dtype, int64_t n_feat_rows, int64_t C,
+                           double feat_scale,
+                           const int32_t *ranks_depth, const int32_t *ranks_feat,
+                           const int32_t *ranks_bev, int64_t n_points,
+                           const int32_t *interval_starts, const int32_t *interval_lengths,
+                           int64_t n_intervals, int64_t n_cells, int n_threads,
+                           double *out, double *out_abs)
+{
+    if (!check_dtypes(depth_dtype, feat_dtype) || n_threads < 1) return -1;
+    /* the intervals must tile the points in order, one per cell */
+    int64_t next = 0;
+    for (int64_t i = 0; i < n_intervals; ++i) {
+        int64_t st = interval_starts[i], len = interval_lengths[i];
+        if (st != next || len < 1 || st + len > n_points) return -1;
+        for (int64_t t = st + 1; t < st + len; ++t)
+            if (ranks_bev[t] != ranks_bev[st]) return -1;
+        if (i > 0 && ranks_bev[st] <= ranks_bev[st - 1]) return -1;
+        next = st + len;
     }
-    return 0;
+    if (next != n_points) return -1;
+
+    oracle_fwd_args a = {depth, depth_dtype, n_depth, feat, feat_dtype, n_feat_rows, C,
+                         feat_scale, ranks_depth, ranks_feat, ranks_bev, n_cells, out, out_abs};
+    memset(out, 0, (size_t)(n_cells * C) * sizeof(double));
+    if (out_abs) memset(out_abs, 0, (size_t)(n_cells * C) * sizeof(double));
+    if (n_threads > n_intervals) n_threads = n_intervals > 0 ? (int)n_intervals : 1;
+
+    oracle_range *rs = (oracle_range *)calloc((size_t)n_threads, sizeof(oracle_range));
+    pthread_t *th = (pthread_t *)calloc((size_t)n_threads, sizeof(pthread_t));
+    if (!rs || !th) { free(rs); free(th); return -2; }
+    int64_t iv = 0;
+    for (int k = 0; k < n_threads; ++k) {
+        int64_t end = n_points * (k + 1) / n_threads;
+        rs[k].a = &a;
+        rs[k].t_lo = iv < n_intervals ? interval_starts[iv] : n_points;
+        while (iv < n_intervals && interval_starts[iv] + interval_lengths[iv] <= end) ++iv;
+        if (k == n_threads - 1) iv = n_intervals;
+        rs[k].t_hi = iv < n_intervals ? interval_starts[iv] : n_points;
+    }
+    int started = 0, status = 0;
+    for (; started < n_threads; ++started)
+        if (pthread_create(&th[started], NULL, sum_range, &rs[started]) != 0) {
+            status = -2;
+            break;
+        }
+    for (int k = 0; k < started; ++k) {
+        pthread_join(th[k], NULL);
+        if (rs[k].status) status = rs[k].status;
+    }
+    free(rs);
+    free(th);
+    return status;
 }
 
 /*

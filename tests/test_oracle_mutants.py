@@ -13,17 +13,17 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "bevpool_oracle.c")
 
 # (name, text in the oracle source, replacement)
 MUTANTS = [
-    ("dropped_last_point", "for (int64_t t = 0; t < n_points; ++t) {",
-     "for (int64_t t = 0; t + 1 < n_points; ++t) {"),
-    ("wrong_sign", "out[rb * C + c] += term;", "out[rb * C + c] -= term;"),
-    ("transposed_feat", "load_value(feat, feat_dtype, rf * C + c)",
-     "load_value(feat, feat_dtype, c * n_feat_rows + rf)"),
+    ("dropped_last_point", "for (int64_t t = t_lo; t < t_hi; ++t) {",
+     "for (int64_t t = t_lo; t + 1 < t_hi; ++t) {"),
+    ("wrong_sign", "a->out[rb * C + c] += term;", "a->out[rb * C + c] -= term;"),
+    ("transposed_feat", "load_value(a->feat, a->feat_dtype, rf * C + c)",
+     "load_value(a->feat, a->feat_dtype, c * a->n_feat_rows + rf)"),
     ("feat_row_uses_W", "ranks_feat[t] = (int32_t)((p / dhw) * hw + p % hw);",
      "ranks_feat[t] = (int32_t)((p / dhw) * hw + p % W);"),
     ("feat_row_drops_image", "ranks_feat[t] = (int32_t)((p / dhw) * hw + p % hw);",
      "ranks_feat[t] = (int32_t)(p % hw);"),
-    ("depth_index_is_row", "double d = load_value(depth, depth_dtype, rd);",
-     "double d = load_value(depth, depth_dtype, rf);"),
+    ("depth_index_is_row", "double d = load_value(a->depth, a->depth_dtype, rd);",
+     "double d = load_value(a->depth, a->depth_dtype, rf);"),
     ("ties_by_descending_p", "if (x->p != y->p) return x->p < y->p ? -1 : 1;",
      "if (x->p != y->p) return x->p < y->p ? 1 : -1;"),
     ("length_off_by_one",
@@ -33,8 +33,8 @@ MUTANTS = [
     ("f16_subnormal_scale", "v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
     ("e4m3_bias", "v = ldexp(8.0 + m, e - 10);", "v = ldexp(8.0 + m, e - 11);"),
     ("e4m3_nan_code", "if (e == 15 && m == 7)", "if (e == 15)"),
-    ("fp8_scale_ignored", "double fscale = feat_dtype == ORACLE_E4M3 ? feat_scale : 1.0;",
-     "double fscale = 1.0;"),
+    ("fp8_scale_ignored", "return feat_dtype == ORACLE_E4M3 ? feat_scale : 1.0;",
+     "return 1.0;"),
     ("first_point_kept_regardless", "if (point_cell[p] >= 0) { keys[k].cell",
      "if (point_cell[p] >= 0 || p == 0) { keys[k].cell"),
     ("segment_skips_last_point", "for (int64_t t = offsets[s]; t < offsets[s + 1]; ++t) {",
@@ -76,7 +76,8 @@ def test_mutant_is_caught(workdir, name, old, new):
     with open(path, "w") as f:
         f.write(src.replace(old, new))
     so = os.path.join(workdir, f"lib_{name}.so")
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", so, path, "-lm"])
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-o", so,
+                           path, "-lm"])
     tests = os.path.dirname(os.path.abspath(__file__))
     code = RUNNER.format(root=os.path.dirname(tests), tests=tests, so=so)
     # a child process, so a mutant that corrupts memory is caught by its crash
