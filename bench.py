@@ -7,9 +7,21 @@ headers, index and depth reads, feature-row gathers, fp32 accumulation,
 owned-row and empty-cell stores) over one frame of synthetic input.  The
 scatter map is built once beforehand (it is prepared once per geometry; its
 build time is reported separately).  Inputs are resident in HBM before
-timing starts.  The K timed steps run as HIP-graph replays of back-to-back
-forward calls on one stream, bracketed by device synchronisation and timed
-with HIP events on that stream.
+timing starts.
+
+Timing.  After the W warm-up steps, the K timed steps are eager launches on
+one stream, bracketed by device synchronisation and timed with HIP events on
+that stream.  Before the start event the stream gets a busy lead-in (a
+bounded spin kernel) long enough for the host to queue all K launches behind
+it, so the events time the steps' GPU work back to back, not the host's
+submission.  A burst of calls still pays its first call's ramp and its last
+call's drain once (a lone call takes about 8 us of GPU time), so a short run
+reads higher per call than a long one.  The JSON line also reports HIP-graph
+replays (graphs of 50 calls in steady state, single 20-call replays, one-call
+graphs back to back: a graph node's dispatch costs the GPU about 0.3 us less
+than an eager launch's, but each replay pays 4-5 us at its boundaries and a
+new graph's first replays run slower), eager launches without the lead-in,
+single-call latencies and a cold-cache call.
 
 Prints ONE JSON line.  value = effective bandwidth in GB/s of the
 algorithmic bytes
@@ -28,6 +40,8 @@ import platform
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -41,12 +55,10 @@ ELEM_BYTES = {"f32": 4, "f16": 2, "e4m3": 1}
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", type=int, default=1, help="synthetic workload 0..4 (1 = headline)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--graph-chunk", type=int, default=50, help="forward calls per captured graph")
-    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
     ap.add_argument("--bags", type=int, default=None,
                     help="benchmark bevpool_segment_reduce on embedding-bag workload k instead")
     ap.add_argument("--kernel", choices=["owned", "v2", "v2do"], default="owned",
@@ -55,6 +67,9 @@ def parse():
                     help="output type of the owned kernel (f16/bf16 via bevpool_forward_ex)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-oracle sample length")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="only the warm-up and timed steps (for profiler runs: the secondary "
+                         "figures include cold-cache calls, which would skew per-dispatch counters)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--details", default=None, help="write extra measurements as JSON here")
@@ -153,12 +168,14 @@ def summarize(args):
     lines = [f"# {name} on {workload} (MI355X, gfx950)", "",
              "Commands (from the repository root):", "", "```", args.commands.strip(), "```", "",
              "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+             "(spin_kernel is the bounded lead-in that the timed steps queue behind.)", "",
              "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
     for r in stats[:8]:
         lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
                      f"{r['MinNs']} | {r['MaxNs']} |")
     lines += ["", "## Benchmark line (same build)", "",
-              f"- per call (HIP events, graph replay): {bench['us_per_call']} us",
+              f"- per call (HIP events over the timed steps, eager launches queued behind a "
+              f"lead-in): {bench['us_per_call']} us",
               f"- rocprof average kernel duration: {avg_ns / 1e3:.3f} us" if avg_ns else "- rocprof: n/a",
               f"- rocprof per-dispatch median {med_ns / 1e3:.3f} us, 10th percentile "
               f"{p10_ns / 1e3:.3f} us over {len(durs)} dispatches (start-to-end timestamps, "
@@ -202,28 +219,68 @@ def summarize(args):
     print(f"wrote {out_md} and {TRAFFIC_FILE}")
 
 
+def host_threads() -> int:
+    """Host cores this process may use: its CPU affinity, capped by
+    OMP_NUM_THREADS when that is set (the share of a shared host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def _median_time(fn, runs, budget_s):
+    """Median wall time of fn over `runs` calls (fewer if budget_s runs out
+    first, at least 3)."""
+    times, t_all = [], time.perf_counter()
+    for i in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+        if i >= 2 and time.perf_counter() - t_all > budget_s:
+            break
+    return float(np.median(times)), len(times)
+
+
 def cpu_baseline(wl, b_alg, seconds):
-    """The oracle's scatter-reduce timed on the host, on a map it builds
-    itself from the same seeded geometry."""
+    """The oracle timed on the host: its fp64 scatter-reduce on one core
+    (oracle.forward) and on all the host cores this process may use
+    (oracle.forward_threads: whole intervals per thread, bitwise the same
+    result), each the median of 20 full calls on the workload, and its map
+    build (median of 20)."""
     import oracle
     oracle.build(force=False)
     s = wl.spec
-    tm = time.perf_counter()
-    ref_map = oracle.build_map(wl.point_cell, s.n_img, s.D, s.H, s.W, s.n_cells)
-    map_ms = (time.perf_counter() - tm) * 1e3
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.forward(wl.depth, wl.feat, s.feat_dtype, wl.feat_scale, s.C, ref_map, s.n_cells)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    per = el / reps
-    return {"value": round(b_alg / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full passes of the oracle's fp64 scatter-reduce over the "
-                      f"{s.name} workload (N={ref_map['n_points']}), {el:.1f} s, single thread",
-            "us_per_call": round(per * 1e6, 1),
-            "map_build_ms": round(map_ms, 1),
+    runs = 5 if s.n_frustum > 1_000_000 else 20
+    box = {}
+
+    def build():
+        box["m"] = oracle.build_map(wl.point_cell, s.n_img, s.D, s.H, s.W, s.n_cells)
+
+    map_s, map_n = _median_time(build, runs, seconds / 4)
+    m = box["m"]
+    one_s, one_n = _median_time(lambda: oracle.forward(wl.depth, wl.feat, s.feat_dtype,
+                                                       wl.feat_scale, s.C, m, s.n_cells),
+                                runs, seconds / 2)
+    threads = host_threads()
+    all_s, all_n = _median_time(lambda: oracle.forward_threads(wl.depth, wl.feat, s.feat_dtype,
+                                                               wl.feat_scale, s.C, m, s.n_cells,
+                                                               threads),
+                                runs, seconds / 4)
+    return {"value": round(b_alg / all_s / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the whole {s.name} workload (N={m['n_points']}, C={s.C}): median of "
+                      f"{all_n} full fp64 scatter-reduce calls on {threads} threads (whole "
+                      f"intervals per thread) and of {one_n} on one thread; map build median "
+                      f"of {map_n}",
+            "us_per_call": round(all_s * 1e6, 1),
+            "single_core": {"value": round(b_alg / one_s / 1e9, 4), "unit": "GB/s",
+                            "us_per_call": round(one_s * 1e6, 1), "cores": 1},
+            "map_build_ms": round(map_s * 1e3, 2),
+            "hardware_concurrency": os.cpu_count(),
             "cpu": _cpu_model()}
 
 
@@ -274,38 +331,21 @@ def bench_bags(args):
     b_alg = N * (s.C * ELEM_BYTES[s.table_dtype] + e_w + 4) + 4 * (s.n_bags + 1) + s.n_bags * s.C * 4
     lib = dws._load()
     stream = torch.cuda.current_stream()
+    a = dws.segment_reduce_args(w, table, idx, off, out, b.table_scale, stream)
+    lead = LeadIn(stream)
     for _ in range(args.warmup):
-        dws.bevpool_segment_reduce(w, table, idx, off, b.table_scale, out)
+        if lib.bevpool_segment_reduce(*a) != 0:
+            raise RuntimeError("bevpool_segment_reduce failed")
     K = args.steps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if args.eager:
-        chunk = None
-        a = dws.segment_reduce_args(w, table, idx, off, out, b.table_scale, stream)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(K):
-            if lib.bevpool_segment_reduce(*a) != 0:
-                raise RuntimeError("bevpool_segment_reduce failed")
-        e1.record(stream)
-        torch.cuda.synchronize()
-    else:
-        chunk = max(1, min(args.graph_chunk, K))
-        while K % chunk:
-            chunk -= 1
-        cap = torch.cuda.Stream()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=cap):
-            a = dws.segment_reduce_args(w, table, idx, off, out, b.table_scale, cap)
-            for _ in range(chunk):
-                if lib.bevpool_segment_reduce(*a) != 0:
-                    raise RuntimeError("bevpool_segment_reduce failed")
-        graph.replay()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(K // chunk):
-            graph.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    lead(lead.cover(K))
+    e0.record(stream)
+    for _ in range(K):
+        if lib.bevpool_segment_reduce(*a) != 0:
+            raise RuntimeError("bevpool_segment_reduce failed")
+    e1.record(stream)
+    torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / K
     gbs = b_alg / (ms * 1e-3) / 1e9
     copy_calibration(args.copy_calib_mib, dev)
@@ -317,7 +357,7 @@ def bench_bags(args):
         "data": "synthetic (geometric bag lengths, skewed rows, N(0,1) table)",
         "config": {"workload": s.name, "bags": s.n_bags, "points": N, "table_rows": s.n_rows,
                    "C": s.C, "table_dtype": s.table_dtype, "weighted": w is not None,
-                   "timing": "eager" if chunk is None else f"hip graph replay, {chunk} calls per graph"},
+                   "timing": "eager launches queued behind a GPU lead-in"},
         "us_per_call": round(ms * 1e3, 3), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -325,6 +365,48 @@ def bench_bags(args):
         "bytes": {"algorithmic": b_alg},
         "secondary": {"copy_calib_mib": args.copy_calib_mib, "kernel_sha256_16": kernel_hash()}}),
         flush=True)
+
+
+def graph_upload(g, stream):
+    """hipGraphUpload of a captured torch graph: its first replay then does
+    not pay the upload inside a timed region."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipGraphUpload.restype = ctypes.c_int
+    hip.hipGraphUpload.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    rc = hip.hipGraphUpload(ctypes.c_void_p(g.raw_cuda_graph_exec()),
+                            ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"hipGraphUpload failed ({rc})")
+
+
+class LeadIn:
+    """A bounded spin kernel (torch.cuda._sleep) enqueued before a start
+    event, long enough for the host to queue the timed calls behind it, so
+    the events time the calls' GPU work and not their submission."""
+
+    US_PER_CALL = 8.0        # host submission budget per queued call (a ctypes launch takes ~3-5 us)
+
+    def __init__(self, stream):
+        import torch
+        self.stream = stream
+        cycles = 1_000_000
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(2):                   # the second measurement is warm
+            torch.cuda.synchronize()
+            e0.record(stream)
+            torch.cuda._sleep(cycles)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        self.cycles_per_us = cycles / max(e0.elapsed_time(e1) * 1e3, 1.0)
+
+    def cover(self, n_calls):
+        """Lead-in length (us) that covers the submission of n_calls launches."""
+        return min(100.0 + self.US_PER_CALL * n_calls, 100_000.0)
+
+    def __call__(self, us):
+        import torch
+        torch.cuda._sleep(max(1000, int(us * self.cycles_per_us)))
 
 
 def main():
@@ -392,88 +474,127 @@ def main():
         if rc != 0:
             raise dws.BevPoolError("bevpool_forward", rc)
 
-    for _ in range(args.warmup):
-        launch()
-    torch.cuda.synchronize()
-
     K = args.steps
-    chunk = max(1, min(args.graph_chunk, K))
-    while K % chunk:
-        chunk -= 1
-    graph = None
-    if not args.eager:
+    lead = LeadIn(stream)
+
+    def capture(n_calls):
+        """A graph of n_calls forward calls, uploaded to the device without
+        running (capture does not run them either)."""
         cap_stream = torch.cuda.Stream()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=cap_stream):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
             gargs = make_args(depth, feat, m, s.n_cells, out, wl.feat_scale, cap_stream)
-            for _ in range(chunk):
+            for _ in range(n_calls):
                 rc = call(gargs)
                 if rc != 0:
                     raise dws.BevPoolError("bevpool_forward", rc)
-        for _ in range(2):
-            graph.replay()
+        graph_upload(g, stream)
         torch.cuda.synchronize()
+        return g
 
-    def timed(n_steps):
+    def timed(n_steps, g=None, per_graph=1, lead_in=True):
+        """(ms, hidden) for n_steps forward calls -- replays of graph g
+        holding per_graph calls, or eager launches -- after a device
+        synchronisation and, with lead_in, a GPU lead-in sized to cover the
+        host's submission of the calls; hidden says whether it did.  (A
+        graph replay is submitted in about 10 us, an eager launch in 3-5.)"""
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        lead_us = lead.cover(n_steps) if lead_in else 0.0
+        if lead_in:
+            lead(lead_us)
+        t0 = time.perf_counter()
         ev0.record(stream)
-        if graph is not None:
-            for _ in range(n_steps // chunk):
-                graph.replay()
+        if g is not None:
+            for _ in range(n_steps // per_graph):
+                g.replay()
         else:
             for _ in range(n_steps):
                 launch()
         ev1.record(stream)
+        host_us = (time.perf_counter() - t0) * 1e6
         torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1)   # ms
+        return ev0.elapsed_time(ev1), host_us < lead_us
 
-    # torch.cuda.graph replays on the current stream, where the events sit
+    # the timed region: exactly K eager steps queued behind the lead-in,
+    # after the W warm-up steps (the only forward calls before them)
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    ms_total = timed(K)
+    ms_total, hidden = timed(K)
     wall_s = time.perf_counter() - t_wall0
     ms_per_step = ms_total / K
     us = ms_per_step * 1e3
     gbs = b_alg / (ms_per_step * 1e-3) / 1e9
 
-    # secondary: median of 100 trials of 20 calls, and eager back-to-back calls
-    trials = []
-    if graph is not None and chunk >= 1:
-        per_trial = chunk * max(1, 20 // chunk) if chunk <= 20 else chunk
-        for _ in range(100):
-            trials.append(timed(per_trial) / per_trial * 1e3)
-    eager_us = None
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(200):
-        launch()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    eager_us = ev0.elapsed_time(ev1) / 200 * 1e3
+    if args.no_secondary:
+        copy_calibration(args.copy_calib_mib, dev)
+        t_s = ms_per_step * 1e-3
+        result = {"metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+                  "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+                  "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+                  "data": "synthetic", "config": {"workload": s.name if not narrow else
+                                                  f"{s.name}_out_{args.out_dtype}"},
+                  "us_per_call": round(us, 3), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                  "bytes": {"algorithmic": b_alg, "compulsory": b_min},
+                  "secondary": {"copy_calib_mib": args.copy_calib_mib,
+                                "kernel_sha256_16": kernel_hash(), "submission_hidden": hidden}}
+        print(json.dumps(result), flush=True)
+        return
 
-    # single-call latency (warm) and cold-cache latency: before each cold call a
-    # 512 MiB buffer is overwritten, which evicts the 256 MB Infinity Cache and
-    # the L2s, so inputs, map and output come from HBM
-    def one_call_us(flush=None):
+    # secondary figures: 50-call graphs in steady state, single 20-call
+    # replays, one-call graphs back to back, eager launches with and without
+    # the lead-in (the host's submission included without it)
+    g50, g20, g1 = capture(50), capture(20), capture(1)
+    for g in (g50, g20, g1):           # a graph's first replays run slower
+        for _ in range(3):
+            g.replay()
+    torch.cuda.synchronize()
+    graph50 = [timed(500, g50, 50)[0] / 500 * 1e3 for _ in range(10)]
+    graph20 = [timed(20, g20, 20)[0] / 20 * 1e3 for _ in range(100)]
+    graph1_us = timed(200, g1, 1)[0] / 200 * 1e3
+    eager_us = timed(500)[0] / 500 * 1e3
+    eager_unhidden_us = timed(500, lead_in=False)[0] / 500 * 1e3
+
+    # single-call latencies (warm): event-bracketed single calls including
+    # the host's submission (eager launch; one-call graph replay), and the
+    # GPU time of one call with the submission hidden; then cold calls: before
+    # each, a 512 MiB buffer is overwritten (its fill also hides the
+    # submission), which evicts the 256 MB Infinity Cache and the L2s, so
+    # inputs, map and output come from HBM
+    def one_call_us(fn=launch, flush=None, lead_in=False):
+        torch.cuda.synchronize()
         if flush is not None:
             flush.fill_(0)
+        if lead_in:
+            lead(100.0)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        launch()
+        fn()
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3
 
     single = [one_call_us() for _ in range(100)]
+    single_g1 = [one_call_us(g1.replay) for _ in range(100)]
+    single_hidden = [one_call_us(lead_in=True) for _ in range(100)]
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    cold = [one_call_us(flush) for _ in range(30)]
+    cold = [one_call_us(flush=flush) for _ in range(30)]
     del flush
 
     copy_calibration(args.copy_calib_mib, dev)
 
     workload_key = s.name if not narrow else f"{s.name}_out_{args.out_dtype}"
     traffic = traffic_for(workload_key)
+    t_s = ms_per_step * 1e-3
+    med = lambda v: round(float(np.median(v)), 3)
+    roofline = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                # HBM bytes actually moved (counters) and the compulsory bytes
+                # (every tensor once), each per call time, as fractions of peak
+                "hbm_frac": round(traffic / t_s / 1e9 / HBM_PEAK_GBS, 4) if traffic else None,
+                "compulsory_frac": round(b_min / t_s / 1e9 / HBM_PEAK_GBS, 4)}
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -492,24 +613,27 @@ def main():
                    "scatter_points": N, "intervals": I, "feat_dtype": s.feat_dtype,
                    "depth_dtype": s.depth_dtype, "out_dtype": args.out_dtype,
                    "kernel": args.kernel,
-                   "timing": "eager" if graph is None else
-                   f"hip graph replay, {chunk} calls per graph"},
+                   "timing": "eager launches queued behind a GPU lead-in"},
         "us_per_call": round(us, 3),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+        "roofline": roofline,
         "bytes": {"algorithmic": b_alg, "compulsory": b_min,
-                  "compulsory_GBps": round(b_min / (ms_per_step * 1e-3) / 1e9, 2)},
-        "secondary": {"median_us_100x20": round(float(np.median(trials)), 3) if trials else None,
-                      "p10_us": round(float(np.percentile(trials, 10)), 3) if trials else None,
-                      "p90_us": round(float(np.percentile(trials, 90)), 3) if trials else None,
-                      "eager_back_to_back_us": round(eager_us, 3),
-                      "single_call_us_median": round(float(np.median(single)), 3),
-                      "cold_call_us_median": round(float(np.median(cold)), 3),
+                  "compulsory_GBps": round(b_min / t_s / 1e9, 2)},
+        "secondary": {"submission_hidden": hidden,
+                      "graph50_replay_us_median": med(graph50),
+                      "graph20_replay_us_median": med(graph20),
+                      "graph20_replay_p10_us": round(float(np.percentile(graph20, 10)), 3),
+                      "graph20_replay_p90_us": round(float(np.percentile(graph20, 90)), 3),
+                      "graph1_back_to_back_us": round(graph1_us, 3),
+                      "eager_us": round(eager_us, 3),
+                      "eager_unhidden_us": round(eager_unhidden_us, 3),
+                      "single_call_us_median": med(single),
+                      "single_call_graph1_us_median": med(single_g1),
+                      "single_call_gpu_us_median": med(single_hidden),
+                      "cold_call_us_median": med(cold),
                       "cold_GBps": round(b_alg / (float(np.median(cold)) * 1e-6) / 1e9, 1),
                       "map_build_ms": round(map_ms, 3),
-                      "timed_region_wall_s": round(wall_s, 3),
+                      "timed_region_wall_s": round(wall_s, 6),
                       "copy_calib_mib": args.copy_calib_mib,
                       "kernel_sha256_16": kernel_hash()},
     }

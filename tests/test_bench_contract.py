@@ -38,6 +38,24 @@ def test_bench_prints_one_json_line():
     assert set(rf) >= {"bound", "achieved", "peak", "unit", "frac", "traffic"}
     assert rf["bound"] == "hbm" and rf["peak"] == 8000.0
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    assert 0 < rf["compulsory_frac"] <= rf["frac"]
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["sample"]
+    assert cb["single_core"]["cores"] == 1 and cb["hardware_concurrency"] >= cb["cores"]
     assert d["config"]["workload"] == "tiny"
+
+
+def test_cpu_baseline_fields():
+    """The CPU leg alone (no GPU needed): one-core and all-core oracle
+    medians on the same workload, with the thread count it used."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads
+    wl = workloads.make_workload(0)
+    s = wl.spec
+    b_alg, _ = bench.algorithmic_bytes(s, int((wl.point_cell >= 0).sum()), 37)
+    cb = bench.cpu_baseline(wl, b_alg, 1.0)
+    assert cb["kind"] == "oracle" and cb["unit"] == "GB/s"
+    assert cb["cores"] == bench.host_threads() >= 1
+    assert cb["value"] > 0 and cb["single_core"]["value"] > 0 and cb["map_build_ms"] > 0
+    assert cb["hardware_concurrency"] >= 1 and cb["cpu"]
