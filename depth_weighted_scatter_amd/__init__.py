@@ -17,7 +17,8 @@ import torch
 
 __all__ = ["BevPoolError", "BevMap", "F32", "F16", "FP8_E4M3", "MAX_TABLE_BYTES", "library_path",
            "bevpool_status_string", "bevpool_version", "bevpool_build_map_workspace_size",
-           "bevpool_build_map", "bevpool_forward", "bevpool_forward_baseline", "forward_args",
+           "bevpool_build_map", "bevpool_build_map_no_alloc", "NO_ALLOC_MAP_SCRATCH_BYTES",
+           "bevpool_forward", "bevpool_forward_baseline", "forward_args",
            "bevpool_forward_ex", "forward_ex_args", "BF16",
            "bevpool_segment_reduce", "segment_reduce_args",
            "ORDER_TILE_OUTER", "ORDER_DEPTH_OUTER"]
@@ -28,6 +29,8 @@ _LIB_PATH = os.path.join(_PKG, "libbevpool.so")
 F32, F16, FP8_E4M3, BF16 = 0, 1, 2, 3
 # largest feature (or segment) table in bytes, BEVPOOL_MAX_TABLE_BYTES in bevpool.h
 MAX_TABLE_BYTES = 2 ** 32 - 4096
+# static device workspace of bevpool_build_map_no_alloc, BEVPOOL_NO_ALLOC_MAP_SCRATCH_BYTES
+NO_ALLOC_MAP_SCRATCH_BYTES = 80 << 20
 ORDER_TILE_OUTER, ORDER_DEPTH_OUTER = 0, 1
 OK, ERR_CAPACITY = 0, -5
 
@@ -69,6 +72,10 @@ def _load():
                                       vp, vp, vp, vp, vp, i64,
                                       ctypes.POINTER(i32), ctypes.POINTER(i32),
                                       vp, sz, vp]
+    lib.bevpool_build_map_no_alloc.restype = ctypes.c_int
+    lib.bevpool_build_map_no_alloc.argtypes = [vp, i32, i32, i32, i32, i64,
+                                               vp, vp, vp, vp, vp, i64,
+                                               ctypes.POINTER(i32), ctypes.POINTER(i32), vp]
     lib.bevpool_forward.restype = ctypes.c_int
     lib.bevpool_forward.argtypes = [vp, i32, i64, vp, i32, i64, i32, ctypes.c_float,
                                     vp, vp, vp, vp, vp, i32, i32, vp, i64, vp]
@@ -152,6 +159,38 @@ def bevpool_build_map(point_cell: torch.Tensor, n_img: int, D: int, H: int, W: i
         raise BevPoolError("bevpool_build_map", rc)
     N, I = n_pts.value, n_iv.value
     return BevMap(arrs[0][:N], arrs[1][:N], arrs[2][:N], arrs[3][:I], arrs[4][:I], N, I)
+
+
+def bevpool_build_map_no_alloc(point_cell: torch.Tensor, n_img: int, D: int, H: int, W: int,
+                               n_cells: int, arrays: Optional[list] = None,
+                               stream=None) -> BevMap:
+    """bevpool_build_map with the library's static device workspace: no
+    workspace is allocated.  arrays: the five int32 output tensors
+    (ranks_depth, ranks_feat, ranks_bev, interval_starts, interval_lengths),
+    each of the same capacity; allocated here (n_img*D*H*W entries each) when
+    None.  Calls on one device share the workspace: do not overlap them."""
+    lib = _load()
+    _check_device_tensor("point_cell", point_cell, torch.int32)
+    P = n_img * D * H * W
+    if point_cell.numel() != P:
+        raise ValueError(f"point_cell has {point_cell.numel()} entries, expected {P}")
+    if arrays is None:
+        arrays = [torch.empty(max(P, 1), dtype=torch.int32, device=point_cell.device)
+                  for _ in range(5)]
+    if len(arrays) != 5:
+        raise ValueError("arrays must hold the five map arrays")
+    for a in arrays:
+        _check_device_tensor("map array", a, torch.int32)
+    cap = min(a.numel() for a in arrays)
+    n_pts, n_iv = ctypes.c_int32(), ctypes.c_int32()
+    rc = lib.bevpool_build_map_no_alloc(point_cell.data_ptr(), n_img, D, H, W, n_cells,
+                                        *(a.data_ptr() for a in arrays), cap,
+                                        ctypes.byref(n_pts), ctypes.byref(n_iv),
+                                        _stream_ptr(stream))
+    if rc != OK:
+        raise BevPoolError("bevpool_build_map_no_alloc", rc)
+    N, I = n_pts.value, n_iv.value
+    return BevMap(arrays[0][:N], arrays[1][:N], arrays[2][:N], arrays[3][:I], arrays[4][:I], N, I)
 
 
 def _forward_inputs(depth: torch.Tensor, feat: torch.Tensor, m: BevMap, n_cells: int,

@@ -98,6 +98,34 @@ int bevpool_build_map(const int32_t *point_cell, int32_t n_img, int32_t D, int32
     return BEVPOOL_OK;
 }
 
+int bevpool_build_map_no_alloc(const int32_t *point_cell, int32_t n_img, int32_t D, int32_t H,
+                               int32_t W, int64_t n_cells,
+                               int32_t *ranks_depth, int32_t *ranks_feat, int32_t *ranks_bev,
+                               int32_t *interval_starts, int32_t *interval_lengths,
+                               int64_t capacity, int32_t *h_n_points, int32_t *h_n_intervals,
+                               hipStream_t stream)
+{
+    // the size checks come first, so an oversized frustum is refused before
+    // any HIP call; the remaining checks are bevpool_build_map's
+    if (n_img > 0 && D > 0 && H > 0 && W > 0) {
+        const int64_t P = int64_t(n_img) * D * H * W;
+        if (P <= kInt32Limit && bevpool::map_workspace_bytes(P) > bevpool::kMapScratchBytes)
+            return BEVPOOL_ERR_WORKSPACE;
+    }
+    if (!point_cell || !ranks_depth || !ranks_feat || !ranks_bev || !interval_starts ||
+        !interval_lengths || !h_n_points || !h_n_intervals)
+        return BEVPOOL_ERR_INVALID_ARG;
+    if (n_img <= 0 || D <= 0 || H <= 0 || W <= 0 || n_cells <= 0 || capacity < 0)
+        return BEVPOOL_ERR_INVALID_ARG;
+    if (int64_t(n_img) * D * H * W > kInt32Limit || n_cells > kInt32Limit)
+        return BEVPOOL_ERR_OVERFLOW;
+    void *ws = nullptr;
+    if (bevpool::map_scratch(&ws) != hipSuccess) return BEVPOOL_ERR_HIP;
+    return bevpool_build_map(point_cell, n_img, D, H, W, n_cells, ranks_depth, ranks_feat,
+                             ranks_bev, interval_starts, interval_lengths, capacity, h_n_points,
+                             h_n_intervals, ws, bevpool::kMapScratchBytes, stream);
+}
+
 }  // extern "C"
 
 namespace {

@@ -28,6 +28,14 @@ size_t map_workspace_bytes(int64_t P);
 // intervals, out-of-range cells) sit at h_counts after a stream sync.
 hipError_t run_build_map(const MapParams &p, int32_t h_counts[3], hipStream_t stream);
 
+// Size of the per-device static workspace of bevpool_build_map_no_alloc
+// (BEVPOOL_NO_ALLOC_MAP_SCRATCH_BYTES in bevpool.h).
+constexpr size_t kMapScratchBytes = size_t(80) << 20;
+
+// Device address of the current device's static map workspace (looked up
+// once per device).
+hipError_t map_scratch(void **ptr);
+
 // ---- forward -----------------------------------------------------------------
 enum DType : int32_t { kF32 = 0, kF16 = 1, kE4M3 = 2, kBF16 = 3 };
 

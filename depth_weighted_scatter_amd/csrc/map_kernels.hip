@@ -23,6 +23,8 @@
 //      of consecutive starts.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "bevpool_internal.h"
 
 namespace bevpool {
@@ -229,6 +231,13 @@ __global__ __launch_bounds__(kBlock) void radix_scatter(const int *keys, const i
     }
 }
 
+// Zeroes the build's counters: a kernel rather than a memset, so the
+// sequence holds kernels only.
+__global__ __launch_bounds__(64) void clear_counters(int *counters, int n)
+{
+    if (int(threadIdx.x) < n) counters[threadIdx.x] = 0;
+}
+
 // ---------------------------------------------------------------- emission
 __device__ inline bool starts_interval(const int *keys, int t)
 {
@@ -313,7 +322,8 @@ hipError_t run_build_map(const MapParams &mp, int32_t h_counts[3], hipStream_t s
     Workspace w = carve(mp.workspace, mp.P);
     const int P = mp.P, nb = w.nb_tiles;
     int *counters = w.counters;   // [0] kept, [1] intervals, [2] bad cells, [3] spare total
-    hipError_t e = hipMemsetAsync(counters, 0, 16 * sizeof(int), s);
+    clear_counters<<<1, 64, 0, s>>>(counters, 16);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
     // bits needed for the largest cell index
@@ -357,6 +367,39 @@ hipError_t run_build_map(const MapParams &mp, int32_t h_counts[3], hipStream_t s
         hipSuccess)
         return e;
     return hipStreamSynchronize(s);
+}
+
+// ------------------------------------------------ workspace without allocation
+// For callers that cannot allocate (code under graph capture, serving loops,
+// harnesses that forbid hipMalloc), bevpool_build_map_no_alloc takes its
+// workspace from this array instead of the caller.  Each device the library
+// runs on holds its own copy from the module's load until the process ends.
+// In host code the name stands for a host-side shadow, not a device address:
+// kernels get the device address that hipGetSymbolAddress returns, looked up
+// once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[kMapScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t map_scratch(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace bevpool

@@ -23,7 +23,8 @@
  * Conventions (all calls):
  *   - Pointers without an h_ prefix are device pointers (HBM of the current
  *     device); h_ pointers are host pointers.  The caller owns all memory;
- *     the library allocates nothing and frees nothing.
+ *     the library allocates nothing and frees nothing (the one device array
+ *     it holds, the workspace of bevpool_build_map_no_alloc, is static).
  *   - Every call returns a bevpool_status; no C++ exception crosses the ABI.
  *     Arguments are validated on the host before any HIP call, so a failed
  *     validation touches neither the GPU nor any output.
@@ -121,6 +122,38 @@ int bevpool_build_map(const int32_t *point_cell, int32_t n_img, int32_t D, int32
                       int32_t *interval_starts, int32_t *interval_lengths, int64_t capacity,
                       int32_t *h_n_points, int32_t *h_n_intervals,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Size of the static device workspace of bevpool_build_map_no_alloc: 80 MiB
+ * per device, enough for frustums of up to 4,091,520 points. */
+#define BEVPOOL_NO_ALLOC_MAP_SCRATCH_BYTES (80u << 20)
+
+/*
+ * bevpool_build_map_no_alloc -- bevpool_build_map for callers that cannot
+ * allocate device memory (harnesses that forbid hipMalloc, serving loops
+ * that must not allocate): the workspace is a static device array of the
+ * library (BEVPOOL_NO_ALLOC_MAP_SCRATCH_BYTES on each device the library
+ * runs on, held until the process ends) instead of a caller argument.  It
+ * calls no allocating routine.  The caller still passes the point_cell input
+ * and the five map arrays.
+ *
+ * Arguments, outputs, blocking behaviour and errors are those of
+ * bevpool_build_map without workspace / workspace_bytes, except:
+ *   BEVPOOL_ERR_WORKSPACE when bevpool_build_map_workspace_size() of the
+ *       frustum exceeds BEVPOOL_NO_ALLOC_MAP_SCRATCH_BYTES (checked first, on
+ *       the host, before any HIP call);
+ *   BEVPOOL_ERR_HIP also when the workspace's device address cannot be
+ *       looked up on the current device.
+ * Every call on one device uses that device's one array: calls that overlap
+ * on a device (other host threads, or other streams of the same device) race
+ * and must be serialised by the caller.  The array keeps the previous call's
+ * contents; the build clears what it needs.
+ */
+int bevpool_build_map_no_alloc(const int32_t *point_cell, int32_t n_img, int32_t D, int32_t H,
+                               int32_t W, int64_t n_cells,
+                               int32_t *ranks_depth, int32_t *ranks_feat, int32_t *ranks_bev,
+                               int32_t *interval_starts, int32_t *interval_lengths,
+                               int64_t capacity, int32_t *h_n_points, int32_t *h_n_intervals,
+                               hipStream_t stream);
 
 /*
  * bevpool_forward -- the depth-weighted, interval-owned scatter-reduce

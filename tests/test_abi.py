@@ -166,6 +166,38 @@ def test_build_map_rejects(lib, kw, code):
     assert _map(lib, **kw) == code
 
 
+def _map_no_alloc(lib, **kw):
+    n_pts, n_iv = ctypes.c_int32(), ctypes.c_int32()
+    a = dict(pc=FAKE, n_img=1, D=2, H=2, W=2, n_cells=4, rd=FAKE, rf=FAKE, rb=FAKE, st=FAKE,
+             ln=FAKE, cap=8, hn=ctypes.byref(n_pts), hi=ctypes.byref(n_iv), stream=None)
+    a.update(kw)
+    return lib.bevpool_build_map_no_alloc(*a.values())
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_img=96, D=59, H=32, W=88), -4),      # 15.9 M points: past the 80 MiB workspace
+    (dict(n_img=1, D=1, H=1, W=4091521), -4),    # one point past the largest frustum
+    (dict(pc=None), -1),
+    (dict(ln=None), -1),
+    (dict(D=0), -1),
+    (dict(cap=-1), -1),
+    (dict(n_img=1 << 16, D=1 << 16), -3),        # P >= 2^31
+    (dict(n_cells=1 << 31), -3),
+])
+def test_build_map_no_alloc_rejects(lib, kw, code):
+    assert _map_no_alloc(lib, **kw) == code
+
+
+def test_no_alloc_limit_matches_header(lib):
+    with open(HEADER) as f:
+        m = re.search(r"#define BEVPOOL_NO_ALLOC_MAP_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == dws.NO_ALLOC_MAP_SCRATCH_BYTES
+    # the largest frustum the header names fits, one more point does not
+    assert dws.bevpool_build_map_workspace_size(1, 1, 1, 4091520, 4) <= dws.NO_ALLOC_MAP_SCRATCH_BYTES
+    assert dws.bevpool_build_map_workspace_size(1, 1, 1, 4091521, 4) > dws.NO_ALLOC_MAP_SCRATCH_BYTES
+
+
 @no_gpu_only
 def test_baseline_rejects(lib):
     a = dict(depth=FAKE, ddt=dws.F16, n_depth=100, feat=FAKE, fdt=dws.F16, rows=10, C=80,
