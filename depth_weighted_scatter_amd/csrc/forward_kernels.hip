@@ -360,7 +360,14 @@ __device__ inline typename ChunkVec<CB>::type load_chunk(__amdgpu_buffer_rsrc_t 
 // never wraps past lane 63, and the slots without a point read a zero row
 // (kEmptySlotOffset) with weight zero: every lane accumulates without a
 // branch, exactly (0 * 0 adds +0 whatever the table holds).  Staged loads
-// past the table write zeros to LDS the same way.  Otherwise (PPWC == 0: G
+// past the table write zeros to LDS the same way.  Every slot group of a
+// round is then requested and accumulated unguarded, the last round's empty
+// groups included: with a wave-uniform test per group the compiler could
+// not pair each load with its accumulation across the round loop, and at
+// four or more groups per round it waited for each load before issuing the
+// next (one round trip per group); without the tests the kernels also lose
+// about 90 scalar instructions (3-5 % on the 209K-point frames, up to 8 % on
+// embedding bags).  Otherwise (PPWC == 0: G
 // known at run time; rounds over 64 points; staged rounds under 48 points,
 // which measured faster in 64-point batches than in whole rounds) the lanes
 // past the batch repeat its last point and empty slots are skipped by exec
@@ -432,7 +439,7 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
             V v[SUB];
 #pragma unroll
             for (int u = 0; u < SUB; ++u) {
-                if (s0 + u * s.PPW < nb) {
+                if (ZERO || s0 + u * s.PPW < nb) {
                     if constexpr (ZERO)
                         v[u] = load_chunk<CB>(rows_rsrc, uint32_t(rows[u]) + uint32_t(s.k * CB));
                     else if constexpr (SEG)
@@ -445,7 +452,7 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
             // of staged instruction j at stage + 1024 j + 16 i
 #pragma unroll
             for (int u = SUB; u < SUB + LST; ++u) {
-                if (s0 + u * s.PPW < nb) {
+                if (ZERO || s0 + u * s.PPW < nb) {
                     if constexpr (ZERO)
                         __builtin_amdgcn_raw_ptr_buffer_load_lds(
                             rows_rsrc, (__attribute__((address_space(3))) void *)(stage + (u - SUB) * 1024), 16,
@@ -477,13 +484,13 @@ __device__ inline void accumulate_points(const FwdParams &p, int t0, int n, cons
             for (int u = 0; u < SUB + LST; ++u) ds[u] = __shfl(my_d, (s0 + u * s.PPW + s.g) & (kWave - 1));
 #pragma unroll
             for (int u = 0; u < SUB; ++u) {
-                if (s0 + u * s.PPW < nb) {
+                if (ZERO || s0 + u * s.PPW < nb) {
                     if (ZERO || (s.ok && s0 + u * s.PPW + s.g < nb)) Accum<FT, CB>::run(acc, ds[u], v[u]);
                 }
             }
 #pragma unroll
             for (int u = SUB; u < SUB + LST; ++u) {
-                if (s0 + u * s.PPW < nb) {
+                if (ZERO || s0 + u * s.PPW < nb) {
                     typedef __attribute__((address_space(3))) const V lds_v;
                     const V x = *reinterpret_cast<lds_v *>(stage + (u - SUB) * 1024 + s.lane * 16);
                     if (ZERO || (s.ok && s0 + u * s.PPW + s.g < nb)) Accum<FT, CB>::run(acc, ds[u], x);
