@@ -209,3 +209,111 @@ def test_segment_reduce_exact_every_geometry(table_dtype, C):
                                to_gpu(off), table_scale=scale, out=out)
     torch.cuda.synchronize()
     _assert_exact(out.cpu(), ref, f"segments {table_dtype} C={C}")
+
+
+# ---------------------------------------------------------------- random mixes
+# Channel counts that reach every kind of kernel (compiled chunk counts and the
+# points-per-wave classes, both e4m3 chunk sizes).
+_RANDOM_C = {"f32": [4, 8, 12, 20, 28, 36, 44, 52, 64, 68, 84, 96, 128, 132, 188, 252, 256],
+             "f16": [8, 16, 24, 40, 56, 72, 80, 88, 104, 120, 128, 136, 168, 192, 256, 264,
+                     320, 400, 504, 512],
+             "e4m3": [8, 16, 24, 40, 56, 72, 80, 96, 104, 128, 136, 176, 248, 256, 264, 272,
+                      336, 384, 512, 528, 784, 1024]}
+
+
+def _random_cells(rng, P, n_cells):
+    """Point cells of several shapes: uniform, hot cells (long intervals),
+    clusters with long gaps, one end of the grid, very sparse."""
+    kind = int(rng.integers(0, 5))
+    if kind == 0:
+        pc = rng.integers(0, n_cells, P)
+    elif kind == 1:
+        pc = rng.choice(rng.integers(0, n_cells, 5), P)
+    elif kind == 2:
+        centres = rng.integers(0, n_cells, 4)
+        pc = np.clip(centres[rng.integers(0, 4, P)] + rng.integers(-150, 150, P), 0, n_cells - 1)
+    elif kind == 3:
+        lo = int(rng.integers(0, max(1, n_cells - 400)))
+        pc = rng.integers(lo, min(n_cells, lo + 400), P)
+    else:
+        pc = rng.choice(rng.integers(0, n_cells, max(1, P // 300)), P)
+    pc = pc.astype(np.int32)
+    pc[rng.random(P) < float(rng.choice([0.0, 0.2, 0.6]))] = -1
+    return pc
+
+
+def forward_exact_case(seed):
+    """One random forward case on exact inputs: feature type, channel count,
+    output type, frustum shape, cell pattern, and sometimes a feature table
+    padded past 8 MB (the per-XCD block order); the map is built on the GPU
+    and compared bit for bit, the output too (16-bit outputs against torch's
+    rounding of the exact sum)."""
+    from gpu_util import assert_maps_equal, gpu_map, map_to_numpy
+    rng = np.random.default_rng(50_000 + seed)
+    fdt = str(rng.choice(["f32", "f16", "e4m3"]))
+    C = int(rng.choice(_RANDOM_C[fdt]))
+    odt = [torch.float32, torch.float16, torch.bfloat16][int(rng.integers(0, 3))]
+    n_img = int(rng.integers(1, 4))
+    D, H, Wd = int(rng.integers(1, 20)), int(rng.integers(1, 9)), int(rng.integers(1, 60))
+    P = n_img * D * H * Wd
+    n_cells = int(rng.choice([1, 7, 300, 5000, 60000]))
+    pc = _random_cells(rng, P, n_cells)
+    rows = n_img * H * Wd
+    eb = {"f32": 4, "f16": 2, "e4m3": 1}[fdt]
+    pad = (9 << 20) // (C * eb) + 1 if rng.random() < 0.2 else 0
+    depth = W.power_of_two_weights(rng, P, "f32" if fdt == "f32" else "f16")
+    feat, scale = W.exact_values(rng, (rows + pad, C), fdt)
+    say(f"[exact random forward {seed}] {fdt} C={C} out={str(odt).split('.')[-1]} "
+        f"P={P} cells={n_cells} pad={pad}")
+    ref_map = oracle.build_map(pc, n_img, D, H, Wd, n_cells)
+    m = gpu_map(pc, n_img, D, H, Wd, n_cells)
+    assert_maps_equal(map_to_numpy(m), ref_map, f"seed {seed}")
+    ref = oracle.forward(depth, feat[:rows], fdt, scale, C, ref_map, n_cells)   # padding unread
+    _premises(feat[:rows], fdt, depth, ref)
+    want = torch.from_numpy(ref.astype(np.float32)).to(odt).to(torch.float64).numpy()
+    got = _gpu_forward(depth, feat, scale, m, n_cells, C, odt)
+    _assert_exact(got, want, f"random forward seed {seed}")
+
+
+def segment_exact_case(seed):
+    """One random segment-reduce case on exact inputs: table type and width,
+    weighted or not, bag lengths from empty to past the channel-split limit."""
+    rng = np.random.default_rng(60_000 + seed)
+    tdt = str(rng.choice(["f32", "f16", "e4m3"]))
+    C = int(rng.choice(_RANDOM_C[tdt]))
+    n_seg = int(rng.integers(1, 400))
+    kind = int(rng.integers(0, 3))
+    if kind == 0:
+        lens = rng.integers(0, 40, n_seg)
+    elif kind == 1:
+        lens = rng.geometric(1 / 20, n_seg)
+        lens[rng.random(n_seg) < 0.05] = 0
+    else:
+        lens = rng.integers(0, 10, n_seg)
+        lens[rng.integers(0, n_seg, 3)] = rng.integers(380, 1500, 3)
+    lens = lens.astype(np.int64)
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    rows = int(rng.integers(1, 5000))
+    idx = rng.integers(0, rows, size=max(int(off[-1]), 1)).astype(np.int32)
+    table, scale = W.exact_values(rng, (rows, C), tdt)
+    w = (W.power_of_two_weights(rng, idx.size, "f32" if tdt == "f32" else "f16")
+         if rng.random() < 0.7 else None)
+    say(f"[exact random segments {seed}] {tdt} C={C} segments={n_seg} N={int(off[-1])} "
+        f"weighted={w is not None}")
+    ref = oracle.segment_reduce(w, table, tdt, scale, idx, off)
+    _premises(table, tdt, w, ref)
+    out = torch.full((n_seg, C), float("nan"), dtype=torch.float32, device=dev())
+    dws.bevpool_segment_reduce(to_gpu(w) if w is not None else None, to_gpu(table), to_gpu(idx),
+                               to_gpu(off), table_scale=scale, out=out)
+    torch.cuda.synchronize()
+    _assert_exact(out.cpu(), ref, f"random segments seed {seed}")
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_forward_exact_random_mix(seed):
+    forward_exact_case(seed)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_segment_reduce_exact_random_mix(seed):
+    segment_exact_case(seed)
