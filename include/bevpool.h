@@ -249,8 +249,13 @@ int bevpool_forward_ex(const void *depth, int32_t depth_dtype, int64_t n_depth,
  *   table [n_rows, C] (device, 16-byte aligned), table_dtype and the
  *       supported (weight, table, C) combinations as bevpool_forward.
  *   indices [n_points] int32 rows of table; offsets [n_segments + 1] int32,
- *       non-decreasing, offsets[n_segments] <= n_points.  The kernel trusts
- *       them (values outside the arrays are undefined behaviour).
+ *       non-decreasing, offsets[n_segments] <= n_points.  Row reads are
+ *       bounded by the table's byte size, so no index reads memory outside
+ *       the table: an index from n_rows up to 2^32 / row_bytes, or a small
+ *       negative one (index * row_bytes >= -4096), reads a zero row; any
+ *       other index outside [0, n_rows) reads zeros or an unspecified row.
+ *       Offsets are trusted (values outside the arrays are undefined
+ *       behaviour).
  *   out [n_segments, C] fp32 (device, 16-byte aligned), overwritten.
  * Sizes: n_segments*C and n_rows*C below 2^31, table at most
  * BEVPOOL_MAX_TABLE_BYTES.

@@ -576,3 +576,47 @@ def test_segment_reduce_long_segment_lengths(table_dtype, C):
     got = _gpu_segment_reduce(w, table, scale, idx, off)
     check_forward(got, ref, ref_abs, table_dtype, np.nonzero(lens > 0)[0],
                   f"long segments {table_dtype} C={C}")
+
+
+# Row reads of the segmented reduce are bounded by the table's byte size (the
+# raw buffer's range), so an index outside [0, n_rows) never reads memory
+# outside the table: from n_rows up to 2^32 / row_bytes, and for small
+# negatives, the row reads as zeros.  The expected values come from the
+# oracle on the table with one zero row appended and those indices sent to it.
+PAST_TABLE_ROWS = [("f16", 80), ("f16", 128), ("f16", 48), ("e4m3", 80), ("e4m3", 256),
+                   ("f32", 8)]
+
+
+@pytest.mark.parametrize("table_dtype,C", PAST_TABLE_ROWS,
+                         ids=[f"{a}-C{b}" for a, b in PAST_TABLE_ROWS])
+def test_segment_reduce_index_past_table_reads_zero(table_dtype, C):
+    rng = np.random.default_rng(71 + C)
+    rows = 500
+    lens = np.array([1, 5, 18, 19, 54, 64, 97, 300, 500, 1000, 0, 2])
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    n = int(off[-1])
+    table = rng.standard_normal((rows, C))
+    scale = 1.0
+    if table_dtype == "f32":
+        table, w = table.astype(np.float32), rng.random(n).astype(np.float32)
+    elif table_dtype == "f16":
+        table, w = table.astype(np.float16), rng.random(n).astype(np.float16)
+    else:
+        table, scale = W.quantize_e4m3(table.astype(np.float16))
+        w = rng.random(n).astype(np.float16)
+    row_bytes = table.dtype.itemsize * C
+    idx = rng.integers(0, rows, size=n).astype(np.int64)
+    past = np.array([rows, rows + 1, rows + 123, 1 << 20, (1 << 32) // row_bytes - 1, -1, -3])
+    pick = rng.random(n) < 0.2
+    idx[pick] = rng.choice(past, size=int(pick.sum()))
+    assert idx.max() * row_bytes + row_bytes <= 1 << 32 and idx.min() * row_bytes >= -4096
+    idx = idx.astype(np.int32)
+    zero_row = np.zeros((1, C), dtype=table.dtype)
+    table_ext = np.concatenate([table, zero_row])
+    idx_ref = np.where((idx >= 0) & (idx < rows), idx, rows).astype(np.int32)
+    say(f"[past-table indices {table_dtype} C={C}] N={n} out-of-range={int(pick.sum())}")
+    ref, ref_abs = oracle.segment_reduce(w, table_ext, table_dtype, scale, idx_ref, off,
+                                         with_abs=True)
+    got = _gpu_segment_reduce(w, table, scale, idx, off)
+    check_forward(got, ref, ref_abs, table_dtype, np.nonzero(lens > 0)[0],
+                  f"past-table indices {table_dtype} C={C}")
