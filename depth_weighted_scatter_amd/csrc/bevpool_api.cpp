@@ -16,6 +16,19 @@ constexpr int64_t kTableBytesLimit = int64_t(BEVPOOL_MAX_TABLE_BYTES);
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Frustum points n_img * D * H * W for positive factors, saturated just past
+// the INT32 limit: each step multiplies a value at most 2^31 by a factor
+// below 2^31, so no int64 product overflows however large the factors are.
+int64_t frustum_points(int32_t n_img, int32_t D, int32_t H, int32_t W)
+{
+    int64_t p = n_img;
+    for (const int32_t f : {D, H, W}) {
+        p *= f;
+        if (p > kInt32Limit) return kInt32Limit + 1;
+    }
+    return p;
+}
+
 int elem_bytes(int32_t dtype)
 {
     switch (dtype) {
@@ -52,7 +65,7 @@ size_t bevpool_build_map_workspace_size(int32_t n_img, int32_t D, int32_t H, int
 {
     if (n_img <= 0 || D <= 0 || H <= 0 || W <= 0 || n_cells <= 0 || n_cells > kInt32Limit)
         return 0;
-    const int64_t P = int64_t(n_img) * D * H * W;
+    const int64_t P = frustum_points(n_img, D, H, W);
     if (P > kInt32Limit) return 0;
     return bevpool::map_workspace_bytes(P);
 }
@@ -69,7 +82,7 @@ int bevpool_build_map(const int32_t *point_cell, int32_t n_img, int32_t D, int32
         return BEVPOOL_ERR_INVALID_ARG;
     if (n_img <= 0 || D <= 0 || H <= 0 || W <= 0 || n_cells <= 0 || capacity < 0)
         return BEVPOOL_ERR_INVALID_ARG;
-    const int64_t P = int64_t(n_img) * D * H * W;
+    const int64_t P = frustum_points(n_img, D, H, W);
     if (P > kInt32Limit || n_cells > kInt32Limit) return BEVPOOL_ERR_OVERFLOW;
     if (!aligned(workspace, 256) || workspace_bytes < bevpool::map_workspace_bytes(P))
         return BEVPOOL_ERR_WORKSPACE;
@@ -108,7 +121,7 @@ int bevpool_build_map_no_alloc(const int32_t *point_cell, int32_t n_img, int32_t
     // the size checks come first, so an oversized frustum is refused before
     // any HIP call; the remaining checks are bevpool_build_map's
     if (n_img > 0 && D > 0 && H > 0 && W > 0) {
-        const int64_t P = int64_t(n_img) * D * H * W;
+        const int64_t P = frustum_points(n_img, D, H, W);
         if (P <= kInt32Limit && bevpool::map_workspace_bytes(P) > bevpool::kMapScratchBytes)
             return BEVPOOL_ERR_WORKSPACE;
     }
@@ -117,7 +130,7 @@ int bevpool_build_map_no_alloc(const int32_t *point_cell, int32_t n_img, int32_t
         return BEVPOOL_ERR_INVALID_ARG;
     if (n_img <= 0 || D <= 0 || H <= 0 || W <= 0 || n_cells <= 0 || capacity < 0)
         return BEVPOOL_ERR_INVALID_ARG;
-    if (int64_t(n_img) * D * H * W > kInt32Limit || n_cells > kInt32Limit)
+    if (frustum_points(n_img, D, H, W) > kInt32Limit || n_cells > kInt32Limit)
         return BEVPOOL_ERR_OVERFLOW;
     void *ws = nullptr;
     if (bevpool::map_scratch(&ws) != hipSuccess) return BEVPOOL_ERR_HIP;
@@ -160,7 +173,9 @@ int validate_forward(const void *depth, int32_t depth_dtype, int64_t n_depth, co
     const bool e4m3_small = !tiles16 && feat_dtype == BEVPOOL_FP8_E4M3 && row_bytes <= 512;
     if (row_bytes % (e4m3_small ? 8 : 16) != 0 || row_bytes > 1024) return BEVPOOL_ERR_UNSUPPORTED;
 
-    if (n_cells * C > kInt32Limit || n_feat_rows * C > kInt32Limit || n_depth > kInt32Limit ||
+    // each count is bounded before it is multiplied, so no product overflows
+    if (n_cells > kInt32Limit || n_feat_rows > kInt32Limit || n_depth > kInt32Limit ||
+        n_cells * C > kInt32Limit || n_feat_rows * C > kInt32Limit ||
         n_feat_rows * row_bytes > kTableBytesLimit)
         return BEVPOOL_ERR_OVERFLOW;
     if (!aligned(out, out_dtype == BEVPOOL_F32 ? 16 : 8) || (feat && !aligned(feat, 16)) ||
@@ -265,7 +280,7 @@ int bevpool_segment_reduce(const void *weights, int32_t weight_dtype, const void
     const int64_t row_bytes = int64_t(C) * fe;
     const bool e4m3_small = table_dtype == BEVPOOL_FP8_E4M3 && row_bytes <= 512;
     if (row_bytes % (e4m3_small ? 8 : 16) != 0 || row_bytes > 1024) return BEVPOOL_ERR_UNSUPPORTED;
-    if (int64_t(n_segments) * C > kInt32Limit || n_rows * C > kInt32Limit ||
+    if (n_rows > kInt32Limit || int64_t(n_segments) * C > kInt32Limit || n_rows * C > kInt32Limit ||
         n_rows * row_bytes > kTableBytesLimit)
         return BEVPOOL_ERR_OVERFLOW;
     if (!aligned(out, 16) || !aligned(table, 16) ||

@@ -68,6 +68,9 @@ def test_workspace_size(lib):
     assert dws.bevpool_build_map_workspace_size(0, 1, 1, 1, 10) == 0
     assert dws.bevpool_build_map_workspace_size(1, 1, 1, 1, 0) == 0
     assert dws.bevpool_build_map_workspace_size(1 << 15, 1 << 15, 4, 1, 10) == 0  # P >= 2^31
+    # a frustum whose int64 product n_img*D*H*W would wrap (2^120 -> 0) is still too large
+    assert dws.bevpool_build_map_workspace_size(1 << 30, 1 << 30, 1 << 30, 1 << 30, 10) == 0
+    assert dws.bevpool_build_map_workspace_size(2**31 - 1, 2**31 - 1, 2**31 - 1, 2**31 - 1, 10) == 0
 
 
 FAKE = 1 << 40          # never dereferenced: validation fails first
@@ -108,6 +111,9 @@ def _fwd(lib, **kw):
     (dict(ddt=dws.F32, fdt=dws.F32, rows=(1 << 24) + 1, C=64), -3),   # fp32 table of 4 GiB + 256 B
     (dict(ddt=dws.F32, fdt=dws.F32, rows=16777201, C=64), -3),        # 256 B over the table limit
     (dict(rows=8388601, C=256), -3),            # fp16 table 512 B over the limit, rows*C < 2^31
+    (dict(n_cells=1 << 62, C=8), -3),           # n_cells * C would wrap to 0 in int64
+    (dict(rows=1 << 62, C=64), -3),             # rows * row bytes would wrap to 0
+    (dict(n_depth=1 << 62), -3),
     (dict(out=FAKE + 4), -1),                   # misaligned output
     (dict(feat=FAKE + 8), -1),                  # misaligned features
 ])
@@ -158,6 +164,7 @@ def _map(lib, **kw):
     (dict(n_cells=0), -1),
     (dict(cap=-1), -1),
     (dict(n_img=1 << 16, D=1 << 16), -3),        # P >= 2^31
+    (dict(n_img=1 << 30, D=1 << 30, H=1 << 30, W=1 << 30), -3),   # the int64 product would wrap to 0
     (dict(n_cells=1 << 31), -3),
     (dict(ws_bytes=16), -4),
     (dict(ws=FAKE + 64), -4),                    # workspace not 256-byte aligned
@@ -183,6 +190,7 @@ def _map_no_alloc(lib, **kw):
     (dict(D=0), -1),
     (dict(cap=-1), -1),
     (dict(n_img=1 << 16, D=1 << 16), -3),        # P >= 2^31
+    (dict(n_img=1 << 30, D=1 << 30, H=1 << 30, W=1 << 30), -3),   # the int64 product would wrap to 0
     (dict(n_cells=1 << 31), -3),
 ])
 def test_build_map_no_alloc_rejects(lib, kw, code):
@@ -222,6 +230,7 @@ def test_baseline_rejects(lib):
     (dict(n_seg=1 << 26, C=64), -3),
     (dict(wdt=dws.F32, tdt=dws.F32, rows=1 << 24, C=64), -3),          # fp32 table of 4 GiB
     (dict(wdt=dws.F32, tdt=dws.F32, rows=16777201, C=64), -3),         # 256 B over the table limit
+    (dict(rows=1 << 62, C=64), -3),                                    # rows * row bytes would wrap to 0
     (dict(out=FAKE + 4), -1),
 ])
 def test_segment_reduce_rejects(lib, kw, code):
