@@ -200,6 +200,14 @@ def _forward_inputs(depth: torch.Tensor, feat: torch.Tensor, m: BevMap, n_cells:
     _check_device_tensor("depth", depth)
     _check_device_tensor("feat", feat)
     _check_device_tensor("out", out)
+    for name in ("ranks_depth", "ranks_feat", "ranks_bev"):
+        _check_device_tensor(name, getattr(m, name), torch.int32)
+        if getattr(m, name).numel() < m.n_points:
+            raise ValueError(f"{name} holds fewer than n_points = {m.n_points} entries")
+    for name in ("interval_starts", "interval_lengths"):
+        _check_device_tensor(name, getattr(m, name), torch.int32)
+        if getattr(m, name).numel() < m.n_intervals:
+            raise ValueError(f"{name} holds fewer than n_intervals = {m.n_intervals} entries")
     if depth.dtype not in (torch.float32, torch.float16):
         raise TypeError(f"depth must be float32 or float16, got {depth.dtype}")
     if feat.dtype not in _TORCH_DTYPE_CODE:
@@ -302,6 +310,8 @@ def segment_reduce_args(weights: Optional[torch.Tensor], table: torch.Tensor,
         raise ValueError("out must be [len(offsets) - 1, C]")
     if weights is not None:
         _check_device_tensor("weights", weights)
+        if weights.dtype not in (torch.float32, torch.float16):
+            raise TypeError(f"weights must be float32 or float16, got {weights.dtype}")
         if weights.numel() != indices.numel():
             raise ValueError("weights and indices differ in length")
         wdt, wptr = _TORCH_DTYPE_CODE[weights.dtype], weights.data_ptr()

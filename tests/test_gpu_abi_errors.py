@@ -94,3 +94,26 @@ def test_segment_reduce_and_map_reject_with_real_buffers(bufs):
     assert (bufs["out"] == 7.0).all(), "a rejected call wrote the output"
     # the map arrays were not touched either
     assert bufs["rb"][:5].tolist() == [0, 0, 0, 1, 1] and bufs["ln"][:2].tolist() == [3, 2]
+
+
+def test_binding_rejects_bad_map_tensors(bufs):
+    """The Python binding checks the map's tensors before anything reaches the
+    library: a host tensor, a wrong dtype or an array shorter than its count
+    raises, and the output keeps its sentinel."""
+    import dataclasses
+    b = bufs
+    m = dws.BevMap(b["rd"], b["rf"], b["rb"], b["st"], b["ln"], 5, 2)
+    depth, feat = b["depth"], b["feat"][:800].view(10, 80)
+    out = torch.full((16, 80), 7.0, dtype=torch.float32, device=depth.device)
+    bad = [(TypeError, dataclasses.replace(m, ranks_feat=b["rf"].cpu())),
+           (TypeError, dataclasses.replace(m, ranks_bev=b["rb"].to(torch.int64))),
+           (ValueError, dataclasses.replace(m, ranks_depth=b["rd"][:4])),
+           (ValueError, dataclasses.replace(m, interval_lengths=b["ln"][:1]))]
+    for err, mm in bad:
+        with pytest.raises(err):
+            dws.bevpool_forward(depth, feat, mm, 16, out=out)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()), "a rejected call wrote the output"
+    with pytest.raises(TypeError):
+        dws.bevpool_segment_reduce(b["depth"][:5].to(torch.bfloat16), feat, b["rf"][:5],
+                                   b["st"][:2], out=out[:1])
