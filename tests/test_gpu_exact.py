@@ -317,3 +317,36 @@ def test_forward_exact_random_mix(seed):
 @pytest.mark.parametrize("seed", range(20))
 def test_segment_reduce_exact_random_mix(seed):
     segment_exact_case(seed)
+
+
+# Maps the builder would never emit: the forward assumes nothing of
+# ranks_feat and ranks_depth beyond being indices into the tables, so a
+# caller's own map -- rows and depth bins in any order, repeated inside one
+# interval, shared between cells -- must pool exactly like the oracle.
+HAND_MAP_CASES = [("f16", 80), ("e4m3", 80), ("f32", 8), ("f16", 256), ("e4m3", 256),
+                  ("f16", 48), ("f32", 36)]
+
+
+@pytest.mark.parametrize("feat_dtype,C", HAND_MAP_CASES, ids=_ids(HAND_MAP_CASES))
+def test_forward_exact_on_hand_built_maps(feat_dtype, C):
+    rng = np.random.default_rng(3000 + C + len(feat_dtype))
+    lengths = np.array(SHORT + [101, 128, 200, 385, 700, 1440], dtype=np.int64)
+    rng.shuffle(lengths)
+    n_iv = lengths.size
+    n_cells = 3 * n_iv + 11
+    cells = np.sort(rng.choice(n_cells, size=n_iv, replace=False)).astype(np.int32)
+    starts = np.concatenate([[0], np.cumsum(lengths)[:-1]]).astype(np.int32)
+    N = int(lengths.sum())
+    rows, n_depth = 37, 53                       # few rows and bins: heavy reuse
+    ref_map = {"ranks_bev": np.repeat(cells, lengths).astype(np.int32),
+               "ranks_feat": rng.integers(0, rows, size=N).astype(np.int32),
+               "ranks_depth": rng.integers(0, n_depth, size=N).astype(np.int32),
+               "interval_starts": starts, "interval_lengths": lengths.astype(np.int32),
+               "n_points": N, "n_intervals": n_iv}
+    depth = W.power_of_two_weights(rng, n_depth, "f32" if feat_dtype == "f32" else "f16")
+    feat, scale = W.exact_values(rng, (rows, C), feat_dtype)
+    say(f"[hand-built map {feat_dtype} C={C}] points={N} intervals={n_iv}")
+    ref = oracle.forward(depth, feat, feat_dtype, scale, C, ref_map, n_cells)
+    _premises(feat, feat_dtype, depth, ref)
+    got = _gpu_forward(depth, feat, scale, map_from_numpy(ref_map), n_cells, C)
+    _assert_exact(got, ref, f"hand-built map {feat_dtype} C={C}")
